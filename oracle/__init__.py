@@ -1,0 +1,182 @@
+"""fp64 CPU oracle for exact masked row-softmax attention (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this package.  It wraps ``oracle.c`` (plain C, IEEE double, OpenMP
+over rows) through ctypes and shares no code with the HIP library.
+
+What each function follows (page title, then the named item on it):
+
+* ``fwd``        -- alphabetamath, "Exact tiled attention and memory-aware
+  differentiation", Theorem "Tiled attention and its recomputed reverse pass
+  are exact": the dense masked attention row, max-shifted as in proof step 2.1.
+* ``bwd``        -- the same page, Algorithm "Exact tiled softmax attention with
+  block-recomputed vector-Jacobian products", reverse procedure, written per
+  output element as in proof steps 4.1-6.1.
+* ``summary`` / ``merge`` -- the same page, Definition "Stable summary of an
+  attention key block" (the summary and its merge).
+* ``fwd_tiled``  -- the Algorithm's forward procedure with key-block size b.
+  ``broken=True`` plants the mistake of Night School "Fused attention",
+  section "Forget one step" (no shrink of the running total).
+
+Inputs are numpy arrays (any float dtype; converted to float64, which is exact
+for fp16/bf16/fp32 values), shaped ``[..., n, d]`` with leading dims flattened
+into independent heads.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+MASKS = {"none": 0, "causal": 1, "window": 2}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (no fast-math, baseline x86-64: no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-Wall", "-o", tmp, _SRC, "-lm"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64, dbl, ip = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.oracle_fwd.argtypes = [i64, i64, i64, i64, ip, ip, ip, dbl, ctypes.c_int, i64, ip,
+                                   i64, ip, ip, ip, ip]
+        lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [i64, i64, i64, i64, ip, ip, ip, ip, dbl, ctypes.c_int, i64,
+                                   ip, ip, ip, ip, ip, ip]
+        lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_summary.argtypes = [i64, i64, ip, ip, ip, ip, ip]
+        lib.oracle_summary.restype = ctypes.c_int
+        lib.oracle_merge.argtypes = [i64, dbl, dbl, ip, dbl, dbl, ip, ctypes.c_int, ip, ip, ip]
+        lib.oracle_merge.restype = ctypes.c_int
+        lib.oracle_fwd_tiled.argtypes = [i64, i64, i64, i64, ip, ip, ip, dbl, ctypes.c_int, i64,
+                                         i64, ctypes.c_int, ip, ip, ip]
+        lib.oracle_fwd_tiled.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _mask_code(mask) -> int:
+    return MASKS[mask] if isinstance(mask, str) else int(mask)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def fwd(q, k, v, scale: float, mask="none", window: int = 0, rows=None):
+    """Dense forward. Returns (Y, M, L, LSE); Y is [..., len(rows), dv]."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2:]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if lead else 1
+    if rows is None:
+        rows_arr, nrows, rp = None, n, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows, rp = len(rows_arr), _ptr(rows_arr)
+    y = np.empty((nh, nrows, dv))
+    m = np.empty((nh, nrows))
+    l = np.empty((nh, nrows))
+    lse = np.empty((nh, nrows))
+    _check(lib.oracle_fwd(nh, n, d, dv, _ptr(q), _ptr(k), _ptr(v), float(scale), _mask_code(mask),
+                          int(window), rp, nrows, _ptr(y), _ptr(m), _ptr(l), _ptr(lse)), "fwd")
+    shp = lead + (nrows,)
+    return y.reshape(shp + (dv,)), m.reshape(shp), l.reshape(shp), lse.reshape(shp)
+
+
+def bwd(q, k, v, g, scale: float, mask="none", window: int = 0):
+    """Dense VJP of Phi = sum(G * Y). Returns (dQ, dK, dV, Y, delta, LSE)."""
+    lib = _load()
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2:]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if lead else 1
+    dq, dk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    y = np.empty_like(v)
+    delta = np.empty(lead + (n,))
+    lse = np.empty(lead + (n,))
+    _check(lib.oracle_bwd(nh, n, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
+                          _mask_code(mask), int(window), _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(y),
+                          _ptr(delta), _ptr(lse)), "bwd")
+    return dq, dk, dvv, y, delta, lse
+
+
+def summary(s, vrows):
+    """Sigma(S) = (m, l, z) of one nonempty block of scores s with value rows vrows [k, dv]."""
+    lib = _load()
+    s = _f64(s).reshape(-1)
+    vrows = _f64(vrows).reshape(len(s), -1)
+    dv = vrows.shape[1]
+    m, l = ctypes.c_double(), ctypes.c_double()
+    z = np.empty(dv)
+    _check(lib.oracle_summary(len(s), dv, _ptr(s), _ptr(vrows), ctypes.byref(m), ctypes.byref(l),
+                              _ptr(z)), "summary")
+    return m.value, l.value, z
+
+
+def merge(a, b, broken: bool = False):
+    """Sigma(S) * Sigma(T) for summaries a = (mS, lS, zS), b = (mT, lT, zT)."""
+    lib = _load()
+    zS, zT = _f64(a[2]).reshape(-1), _f64(b[2]).reshape(-1)
+    m, l = ctypes.c_double(), ctypes.c_double()
+    z = np.empty(len(zS))
+    _check(lib.oracle_merge(len(zS), float(a[0]), float(a[1]), _ptr(zS), float(b[0]), float(b[1]),
+                            _ptr(zT), int(broken), ctypes.byref(m), ctypes.byref(l), _ptr(z)),
+           "merge")
+    return m.value, l.value, z
+
+
+def fwd_tiled(q, k, v, scale: float, mask="none", window: int = 0, block: int = 16,
+              broken: bool = False):
+    """The Algorithm's tiled forward procedure. Returns (Y, M, L)."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2:]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if lead else 1
+    y = np.empty((nh, n, dv))
+    m = np.empty((nh, n))
+    l = np.empty((nh, n))
+    _check(lib.oracle_fwd_tiled(nh, n, d, dv, _ptr(q), _ptr(k), _ptr(v), float(scale),
+                                _mask_code(mask), int(window), int(block), int(broken), _ptr(y),
+                                _ptr(m), _ptr(l)), "fwd_tiled")
+    shp = lead + (n,)
+    return y.reshape(shp + (dv,)), m.reshape(shp), l.reshape(shp)

@@ -1,0 +1,353 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for exact masked row-softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header or constant with the HIP library.
+ *
+ * Sources (cited by page title and the named definition/algorithm/theorem):
+ *  [AM]  alphabetamath.cc, "Exact tiled attention and memory-aware
+ *        differentiation": Definition "Stable summary of an attention key block",
+ *        Algorithm "Exact tiled softmax attention with block-recomputed
+ *        vector-Jacobian products", Theorem "Tiled attention and its recomputed
+ *        reverse pass are exact" (proof steps 1.1-7.1).
+ *  [AI]  igniting.github.io, "The Arithmetic of Intelligence", chapter 12,
+ *        section "Streaming softmax" (the running max / running sum update).
+ *  [NS]  harperz9.github.io, Night School "Fused attention", section
+ *        "Forget one step" (the broken-rescale control).
+ *
+ * Conventions (readings of the pages, also listed in the design notes):
+ *  - Rows and keys are 0-based here; the pages index from 1.
+ *  - Allowed-key sets A_i: mask 0 = all keys; 1 = causal, j <= i (the diagonal
+ *    is allowed); 2 = sliding window of W keys ending at the diagonal,
+ *    max(0, i-W+1) <= j <= i, with W >= 1.  Every such A_i is nonempty, so
+ *    the all-masked row the exactness theorem leaves undefined never occurs.
+ *  - Layout: head-major, row-major, contiguous: Q,K [nh][n][d], V,G,Y [nh][n][dv].
+ *  - All arithmetic is IEEE double; the exponential base is e.
+ *
+ * Functions with a pin (see the tests): every exported function is pinned by
+ * the page's worked examples, closed forms, invariants, finite differences or
+ * a brute-force evaluation.  No function here is "parity unpinned".
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL 1
+#define OR_ENOMEM 2
+
+/* Membership of key j in A_i, read on demand as the Algorithm of [AM] allows. */
+static int in_allowed(int mask, int64_t window, int64_t i, int64_t j)
+{
+    if (mask == 0) return 1;
+    if (mask == 1) return j <= i;
+    return j <= i && j >= i - window + 1;
+}
+
+static int check_args(int64_t nh, int64_t n, int64_t d, int64_t dv, int mask, int64_t window)
+{
+    if (nh < 0 || n < 0 || d < 1 || dv < 1) return OR_EINVAL;
+    if (mask < 0 || mask > 2) return OR_EINVAL;
+    if (mask == 2 && window < 1) return OR_EINVAL;
+    return OR_OK;
+}
+
+/* Score s_ij = c * sum_r Q_ir K_jr  ([AM] Definition, "Stable summary"). */
+static double score(const double *qi, const double *kj, int64_t d, double c)
+{
+    double acc = 0.0;
+    for (int64_t r = 0; r < d; r++) acc += qi[r] * kj[r];
+    return c * acc;
+}
+
+/*
+ * One row of the dense definition ([AM] Theorem "Tiled attention ... are exact",
+ * the displayed dense masked attention row, with the max shift of step 2.1):
+ *   m_i = max_{j in A_i} s_ij,  l_i = sum_{j in A_i} e^{s_ij - m_i},
+ *   Y_i = sum_{j in A_i} (e^{s_ij - m_i} / l_i) V_j.
+ * srow is caller scratch of length n.
+ */
+static void dense_row(const double *Q, const double *K, const double *V, int64_t n, int64_t d,
+                      int64_t dv, double c, int mask, int64_t window, int64_t i, double *srow,
+                      double *y, double *m_out, double *l_out)
+{
+    const double *qi = Q + i * d;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; j++) {
+        if (!in_allowed(mask, window, i, j)) continue;
+        srow[j] = score(qi, K + j * d, d, c);
+        if (srow[j] > m) m = srow[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < n; j++) {
+        if (!in_allowed(mask, window, i, j)) continue;
+        l += exp(srow[j] - m);
+    }
+    for (int64_t a = 0; a < dv; a++) y[a] = 0.0;
+    for (int64_t j = 0; j < n; j++) {
+        if (!in_allowed(mask, window, i, j)) continue;
+        double p = exp(srow[j] - m) / l;
+        const double *vj = V + j * dv;
+        for (int64_t a = 0; a < dv; a++) y[a] += p * vj[a];
+    }
+    *m_out = m;
+    *l_out = l;
+}
+
+/*
+ * Dense forward on nh independent heads.  rows (length nrows) selects which
+ * query rows to evaluate (rows are independent in the definition); rows == NULL
+ * means every row, in order.  Outputs are [nh][nrows][dv] for Y and [nh][nrows]
+ * for M (row max), L (normaliser l) and LSE = m + ln l (natural log).
+ * Any of M, L, LSE may be NULL.
+ */
+int oracle_fwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, const double *K,
+               const double *V, double c, int mask, int64_t window, const int64_t *rows,
+               int64_t nrows, double *Y, double *M, double *L, double *LSE)
+{
+    if (check_args(nh, n, d, dv, mask, window)) return OR_EINVAL;
+    if (rows == NULL) nrows = n;
+    for (int64_t r = 0; rows != NULL && r < nrows; r++)
+        if (rows[r] < 0 || rows[r] >= n) return OR_EINVAL;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *srow = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        if (srow == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int64_t h = 0; h < nh; h++) {
+            for (int64_t r = 0; r < nrows; r++) {
+                if (srow == NULL) continue;
+                int64_t i = rows ? rows[r] : r;
+                const double *Qh = Q + h * n * d, *Kh = K + h * n * d, *Vh = V + h * n * dv;
+                double m, l;
+                dense_row(Qh, Kh, Vh, n, d, dv, c, mask, window, i, srow,
+                          Y + (h * nrows + r) * dv, &m, &l);
+                if (M) M[h * nrows + r] = m;
+                if (L) L[h * nrows + r] = l;
+                if (LSE) LSE[h * nrows + r] = m + log(l);
+            }
+        }
+        free(srow);
+    }
+    return failed ? OR_ENOMEM : OR_OK;
+}
+
+/*
+ * Analytic vector-Jacobian product of Phi = sum_{i,a} G_ia Y_ia, the reverse
+ * procedure of [AM] Algorithm written per output element (proof steps 4.1-6.1):
+ *   p_ij     = e^{s_ij - m_i} / l_i                        (frozen m_i, l_i)
+ *   delta_i  = sum_a G_ia Y_ia
+ *   gamma_ij = p_ij (sum_a G_ia V_ja - delta_i)
+ *   dQ_i     = c sum_{j in A_i} gamma_ij K_j
+ *   dK_j     = c sum_{i : j in A_i} gamma_ij Q_i
+ *   dV_j     = sum_{i : j in A_i} p_ij G_i
+ * Y, M, L come from the dense forward above.  Optional outputs Yout [nh][n][dv],
+ * Dout (delta) and LSEout [nh][n] may be NULL.
+ */
+int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, const double *K,
+               const double *V, const double *G, double c, int mask, int64_t window, double *dQ,
+               double *dK, double *dV, double *Yout, double *Dout, double *LSEout)
+{
+    if (check_args(nh, n, d, dv, mask, window)) return OR_EINVAL;
+    size_t rows_total = (size_t)(nh * n);
+    double *Y = (double *)malloc(sizeof(double) * (rows_total * dv + 1));
+    double *M = (double *)malloc(sizeof(double) * (rows_total + 1));
+    double *L = (double *)malloc(sizeof(double) * (rows_total + 1));
+    double *D = (double *)malloc(sizeof(double) * (rows_total + 1));
+    if (!Y || !M || !L || !D) {
+        free(Y); free(M); free(L); free(D);
+        return OR_ENOMEM;
+    }
+    int rc = oracle_fwd(nh, n, d, dv, Q, K, V, c, mask, window, NULL, n, Y, M, L, NULL);
+    if (rc) {
+        free(Y); free(M); free(L); free(D);
+        return rc;
+    }
+
+    /* delta_i = sum_a G_ia Y_ia */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < (int64_t)rows_total; t++) {
+        double acc = 0.0;
+        for (int64_t a = 0; a < dv; a++) acc += G[t * dv + a] * Y[t * dv + a];
+        D[t] = acc;
+    }
+
+    /* dQ_i: one query row at a time. */
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int64_t h = 0; h < nh; h++) {
+        for (int64_t i = 0; i < n; i++) {
+            const double *Qh = Q + h * n * d, *Kh = K + h * n * d, *Vh = V + h * n * dv;
+            const double *gi = G + (h * n + i) * dv;
+            double m = M[h * n + i], l = L[h * n + i], delta = D[h * n + i];
+            double *dqi = dQ + (h * n + i) * d;
+            for (int64_t r = 0; r < d; r++) dqi[r] = 0.0;
+            for (int64_t j = 0; j < n; j++) {
+                if (!in_allowed(mask, window, i, j)) continue;
+                double p = exp(score(Qh + i * d, Kh + j * d, d, c) - m) / l;
+                double gv = 0.0;
+                for (int64_t a = 0; a < dv; a++) gv += gi[a] * Vh[j * dv + a];
+                double gamma = p * (gv - delta);
+                for (int64_t r = 0; r < d; r++) dqi[r] += c * gamma * Kh[j * d + r];
+            }
+        }
+    }
+
+    /* dK_j and dV_j: one key row at a time, summing over the queries that see it. */
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int64_t h = 0; h < nh; h++) {
+        for (int64_t j = 0; j < n; j++) {
+            const double *Qh = Q + h * n * d, *Kh = K + h * n * d, *Vh = V + h * n * dv;
+            double *dkj = dK + (h * n + j) * d;
+            double *dvj = dV + (h * n + j) * dv;
+            for (int64_t r = 0; r < d; r++) dkj[r] = 0.0;
+            for (int64_t a = 0; a < dv; a++) dvj[a] = 0.0;
+            for (int64_t i = 0; i < n; i++) {
+                if (!in_allowed(mask, window, i, j)) continue;
+                const double *gi = G + (h * n + i) * dv;
+                double m = M[h * n + i], l = L[h * n + i], delta = D[h * n + i];
+                double p = exp(score(Qh + i * d, Kh + j * d, d, c) - m) / l;
+                double gv = 0.0;
+                for (int64_t a = 0; a < dv; a++) gv += gi[a] * Vh[j * dv + a];
+                double gamma = p * (gv - delta);
+                for (int64_t r = 0; r < d; r++) dkj[r] += c * gamma * Qh[i * d + r];
+                for (int64_t a = 0; a < dv; a++) dvj[a] += p * gi[a];
+            }
+        }
+    }
+
+    if (Yout) memcpy(Yout, Y, sizeof(double) * rows_total * dv);
+    if (Dout) memcpy(Dout, D, sizeof(double) * rows_total);
+    if (LSEout)
+        for (size_t t = 0; t < rows_total; t++) LSEout[t] = M[t] + log(L[t]);
+    free(Y); free(M); free(L); free(D);
+    return OR_OK;
+}
+
+/*
+ * Summary Sigma(S) = (m, l, z) of one nonempty block ([AM] Definition "Stable
+ * summary of an attention key block"): from the block's k scores s[] and its k
+ * value rows Vrows [k][dv],
+ *   m = max s,  l = sum e^{s - m},  z = sum e^{s - m} v.
+ */
+int oracle_summary(int64_t k, int64_t dv, const double *s, const double *Vrows, double *m_out,
+                   double *l_out, double *z)
+{
+    if (k < 1 || dv < 0) return OR_EINVAL;
+    double m = -INFINITY;
+    for (int64_t t = 0; t < k; t++)
+        if (s[t] > m) m = s[t];
+    double l = 0.0;
+    for (int64_t a = 0; a < dv; a++) z[a] = 0.0;
+    for (int64_t t = 0; t < k; t++) {
+        double w = exp(s[t] - m);
+        l += w;
+        for (int64_t a = 0; a < dv; a++) z[a] += w * Vrows[t * dv + a];
+    }
+    *m_out = m;
+    *l_out = l;
+    return OR_OK;
+}
+
+/*
+ * Merge Sigma(S) * Sigma(T) of two disjoint nonempty summaries ([AM] Definition):
+ *   m' = max(m_S, m_T), l' = e^{m_S-m'} l_S + e^{m_T-m'} l_T, z' likewise.
+ * broken != 0 plants the mistake of [NS] "Forget one step": the running state
+ * (S, the left operand) is not shrunk, i.e. e^{m_S - m'} is replaced by 1.
+ * Output may alias either input.
+ */
+int oracle_merge(int64_t dv, double mS, double lS, const double *zS, double mT, double lT,
+                 const double *zT, int broken, double *m_out, double *l_out, double *z_out)
+{
+    if (dv < 0) return OR_EINVAL;
+    double mp = mS > mT ? mS : mT;
+    double aS = broken ? 1.0 : exp(mS - mp);
+    double aT = exp(mT - mp);
+    for (int64_t a = 0; a < dv; a++) z_out[a] = aS * zS[a] + aT * zT[a];
+    *l_out = aS * lS + aT * lT;
+    *m_out = mp;
+    return OR_OK;
+}
+
+/*
+ * The forward procedure of [AM] Algorithm, in exact order, with key-block size
+ * b: for each row start from the empty state; for t = 1..ceil(n/b) form
+ * I = J_t cap A_i; skip an empty I; otherwise copy Sigma(I) into an empty
+ * state or merge it in with the merge above; finally Y_i = z_i / l_i and the
+ * row statistics m_i, l_i are retained.  broken is passed to the merge.
+ * Used by the tests to pin the exactness theorem (result independent of b and
+ * equal to the dense rows) and the [NS] control.
+ */
+int oracle_fwd_tiled(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, const double *K,
+                     const double *V, double c, int mask, int64_t window, int64_t b, int broken,
+                     double *Y, double *M, double *L)
+{
+    if (check_args(nh, n, d, dv, mask, window) || b < 1) return OR_EINVAL;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)b);
+        double *vrows = (double *)malloc(sizeof(double) * (size_t)(b * dv));
+        double *zb = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!s || !vrows || !zb) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int64_t h = 0; h < nh; h++) {
+            for (int64_t i = 0; i < n; i++) {
+                if (!s || !vrows || !zb) continue;
+                const double *Qh = Q + h * n * d, *Kh = K + h * n * d, *Vh = V + h * n * dv;
+                double *z = Y + (h * n + i) * dv;
+                int empty = 1; /* the state "bottom" */
+                double m = 0.0, l = 0.0;
+                int64_t nblocks = (n + b - 1) / b;
+                for (int64_t t = 0; t < nblocks; t++) {
+                    int64_t k = 0;
+                    for (int64_t j = t * b; j < (t + 1) * b && j < n; j++) {
+                        if (!in_allowed(mask, window, i, j)) continue;
+                        s[k] = score(Qh + i * d, Kh + j * d, d, c);
+                        memcpy(vrows + k * dv, Vh + j * dv, sizeof(double) * (size_t)dv);
+                        k++;
+                    }
+                    if (k == 0) continue; /* I is empty: leave the state unchanged */
+                    double mb, lb;
+                    oracle_summary(k, dv, s, vrows, &mb, &lb, zb);
+                    if (empty) {
+                        m = mb;
+                        l = lb;
+                        memcpy(z, zb, sizeof(double) * (size_t)dv);
+                        empty = 0;
+                    } else {
+                        oracle_merge(dv, m, l, z, mb, lb, zb, broken, &m, &l, z);
+                    }
+                }
+                for (int64_t a = 0; a < dv; a++) z[a] /= l;
+                if (M) M[h * n + i] = m;
+                if (L) L[h * n + i] = l;
+            }
+        }
+        free(s);
+        free(vrows);
+        free(zb);
+    }
+    return failed ? OR_ENOMEM : OR_OK;
+}
+
+/* Number of OpenMP threads the oracle would use (reported by the benchmark). */
+int oracle_num_threads(void)
+{
+    int t = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        t = omp_get_num_threads();
+    }
+    return t;
+}
