@@ -1,0 +1,6 @@
+"""Exact IO-aware tiled softmax attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in the HIP library built from ``csrc/`` (C ABI in
+``include/eiat_attn.h``); ``attn`` is its Python binding.
+"""
+from .attn import attn_bwd, attn_bwd_workspace_bytes, attn_fwd, load_library  # noqa: F401

@@ -1,0 +1,141 @@
+"""Python binding of the C ABI in include/eiat_attn.h (argument marshalling only).
+
+``attn_fwd`` and ``attn_bwd`` carry the C entry points' names.  PyTorch supplies
+device memory and the stream; every step of the computation runs in the HIP
+kernels of ``libeiat_attn.so``.  There is no fallback: if the library is not
+built, or the tensors are not on a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libeiat_attn.so")
+HEADER = os.path.join(ROOT, "include", "eiat_attn.h")
+
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+MASK_CODES = {"none": 0, "causal": 1, "window": 2}
+STATUS = {0: "EIAT_OK", 1: "EIAT_ERR_INVALID_ARG", 2: "EIAT_ERR_UNSUPPORTED", 3: "EIAT_ERR_HIP"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/eiat_attn.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"EIAT_API[^;(]*?\b(attn_[a-z_]+)\s*\(", text)
+
+
+def load_library():
+    """Load libeiat_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python exact_io_aware_tiled_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, c_int, c_float = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, c_int, c_float, c_int,
+                             i64, vp]
+    lib.attn_fwd.restype = c_int
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
+                             i64, i64, i64, c_int, c_float, c_int, i64, vp]
+    lib.attn_bwd.restype = c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_status_string.argtypes = [c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnError(status, load_library().attn_last_error().decode())
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dims(q: torch.Tensor, v: torch.Tensor):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected [B, H, n, d] tensors")
+    B, H, n, d = q.shape
+    return B, H, n, d, v.shape[-1]
+
+
+def _require(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_fwd(q, k, v, scale: Optional[float] = None, mask: str = "causal", window: int = 0,
+             out=None, lse=None, stream=None):
+    """O, LSE = attention forward.  q, k: [B, H, n, d]; v: [B, H, n, dv] (same dtype)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name)
+    B, H, n, d, dv = _dims(q, v)
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty(B, H, n, dv, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, n, d, dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask],
+                        int(window), _stream_handle(stream)))
+    return out, lse
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, n: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, H, n))
+
+
+def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "causal",
+             window: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of sum(dO * O) given the forward's O and LSE."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do)):
+        _require(t, name)
+    B, H, n, d, dvd = _dims(q, v)
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = attn_bwd_workspace_bytes(B, H, n)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H,
+                        n, d, dvd, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask],
+                        int(window), _stream_handle(stream)))
+    return dq, dk, dv

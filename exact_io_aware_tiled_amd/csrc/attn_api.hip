@@ -1,0 +1,210 @@
+// attn_api.hip -- the C ABI entry points declared in include/eiat_attn.h:
+// argument validation (on the host, before any HIP call), the mapping of the
+// scale c onto the kernels' exponent scale, and dispatch to the kernels.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/eiat_attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+eiat_status fail(eiat_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+eiat_status ok() {
+  g_last_error[0] = '\0';
+  return EIAT_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(int dtype) { return dtype == EIAT_F32 ? 4 : 2; }
+
+// [p, p + bytes) and [r, r + rbytes) share at least one byte.
+bool overlaps(const void* p, size_t bytes, const void* r, size_t rbytes) {
+  if (bytes == 0 || rbytes == 0) return false;
+  uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(r);
+  return a < b + rbytes && b < a + bytes;
+}
+
+// Checks shared by both passes.  On success fills the scale mapping and the
+// clamped window, and sets *empty when there is no work.
+eiat_status check_common(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int dtype,
+                         float scale, int mask, int64_t window, bool* empty, float* qk_scale,
+                         int* qmode, int64_t* win_eff) {
+  if (B < 0 || H < 0 || n < 0) return fail(EIAT_ERR_INVALID_ARG, "B, H and n must be >= 0");
+  if (d < 1 || dv < 1) return fail(EIAT_ERR_INVALID_ARG, "d and dv must be >= 1");
+  if (dtype != EIAT_F32 && dtype != EIAT_F16 && dtype != EIAT_BF16)
+    return fail(EIAT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (mask != EIAT_MASK_NONE && mask != EIAT_MASK_CAUSAL && mask != EIAT_MASK_WINDOW)
+    return fail(EIAT_ERR_INVALID_ARG, "unknown mask kind %d", mask);
+  if (mask == EIAT_MASK_WINDOW && window < 1)
+    return fail(EIAT_ERR_INVALID_ARG, "window must be >= 1 (got %lld)", (long long)window);
+  if (!isfinite(scale)) return fail(EIAT_ERR_INVALID_ARG, "scale must be finite");
+  if (d != dv) return fail(EIAT_ERR_UNSUPPORTED, "d != dv (%lld, %lld) has no kernel", (long long)d, (long long)dv);
+  if (d != 16 && d != 64 && d != 128)
+    return fail(EIAT_ERR_UNSUPPORTED, "head dim %lld has no kernel (16, 64, 128)", (long long)d);
+  // Row indices are 32-bit inside the kernels; grids are at most 2^31 - 1 blocks.
+  if (n > (int64_t)INT32_MAX - 1024) return fail(EIAT_ERR_UNSUPPORTED, "n too large");
+  if (B > 0 && H > (int64_t)INT32_MAX / B) return fail(EIAT_ERR_UNSUPPORTED, "B * H too large");
+  const int64_t bh = B * H;
+  if (bh > 0 && (n + 127) / 128 > (int64_t)INT32_MAX / bh)
+    return fail(EIAT_ERR_UNSUPPORTED, "grid too large");
+  if (bh > 0 && n > 0 && bh > INT64_MAX / n / d / 4)
+    return fail(EIAT_ERR_UNSUPPORTED, "tensor too large");
+  *empty = (bh == 0 || n == 0);
+  if (scale > 0.0f) {
+    *qmode = 0;
+    *qk_scale = (float)((double)scale * 1.4426950408889634);
+  } else if (scale < 0.0f) {
+    *qmode = 1;
+    *qk_scale = (float)(-(double)scale * 1.4426950408889634);
+  } else {
+    *qmode = 2;
+    *qk_scale = 1.0f;
+  }
+  if (!isfinite(*qk_scale)) return fail(EIAT_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+  *win_eff = mask == EIAT_MASK_WINDOW ? (window < n ? window : (n > 0 ? n : 1)) : 0;
+  return EIAT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+eiat_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale, int mask,
+                     int64_t window, void* stream) {
+  bool empty = false;
+  float qk_scale = 1.0f;
+  int qmode = 0;
+  int64_t win = 0;
+  eiat_status s =
+      check_common(B, H, n, d, dv, dtype, scale, mask, window, &empty, &qk_scale, &qmode, &win);
+  if (s != EIAT_OK) return s;
+  if (empty) return ok();
+  if (!q || !k || !v || !o || !lse) return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t eb = elem_bytes(dtype);
+  const size_t qb = (size_t)(B * H * n * d) * eb, vb = (size_t)(B * H * n * dv) * eb;
+  const size_t lb = (size_t)(B * H * n) * 4;
+  const void* ins[3] = {q, k, v};
+  const size_t insz[3] = {qb, qb, vb};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(o, vb, ins[i], insz[i]) || overlaps(lse, lb, ins[i], insz[i]))
+      return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap inputs");
+  if (overlaps(o, vb, lse, lb)) return fail(EIAT_ERR_INVALID_ARG, "o and lse overlap");
+
+  eiat::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = n;
+  a.d = (int)d;
+  a.dtype = dtype;
+  a.mask = mask;
+  a.window = win;
+  a.qk_scale = qk_scale;
+  a.qmode = qmode;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = eiat::launch_fwd(a);
+  if (e != hipSuccess) return fail(EIAT_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n) {
+  if (B <= 0 || H <= 0 || n <= 0) return 0;
+  return (size_t)B * (size_t)H * (size_t)n * sizeof(float);
+}
+
+eiat_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dvv, void* workspace,
+                     size_t workspace_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
+                     int64_t dv, int dtype, float scale, int mask, int64_t window, void* stream) {
+  bool empty = false;
+  float qk_scale = 1.0f;
+  int qmode = 0;
+  int64_t win = 0;
+  eiat_status s =
+      check_common(B, H, n, d, dv, dtype, scale, mask, window, &empty, &qk_scale, &qmode, &win);
+  if (s != EIAT_OK) return s;
+  if (empty) return ok();
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dvv || !workspace)
+    return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
+  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dvv, workspace};
+  for (int i = 0; i < 10; ++i)
+    if (!aligned16(ptrs[i])) return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, H, n))
+    return fail(EIAT_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                attn_bwd_workspace_bytes(B, H, n));
+  const size_t eb = elem_bytes(dtype);
+  const size_t qb = (size_t)(B * H * n * d) * eb, vb = (size_t)(B * H * n * dv) * eb;
+  const size_t lb = (size_t)(B * H * n) * 4;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t insz[6] = {qb, qb, vb, vb, vb, lb};
+  void* outs[4] = {dq, dk, dvv, workspace};
+  const size_t outsz[4] = {qb, qb, vb, attn_bwd_workspace_bytes(B, H, n)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
+        return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap inputs");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
+        return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap each other");
+  }
+
+  eiat::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dvv;
+  a.delta = static_cast<float*>(workspace);
+  a.bh = B * H;
+  a.n = n;
+  a.d = (int)d;
+  a.dtype = dtype;
+  a.mask = mask;
+  a.window = win;
+  a.qk_scale = qk_scale;
+  a.qmode = qmode;
+  a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = eiat::launch_bwd(a);
+  if (e != hipSuccess) return fail(EIAT_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case EIAT_OK: return "EIAT_OK";
+    case EIAT_ERR_INVALID_ARG: return "EIAT_ERR_INVALID_ARG";
+    case EIAT_ERR_UNSUPPORTED: return "EIAT_ERR_UNSUPPORTED";
+    case EIAT_ERR_HIP: return "EIAT_ERR_HIP";
+    default: return "EIAT_UNKNOWN_STATUS";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_abi_version(void) { return EIAT_ABI_VERSION; }
+
+}  // extern "C"

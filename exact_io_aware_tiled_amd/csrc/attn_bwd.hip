@@ -1,0 +1,587 @@
+// attn_bwd.hip -- exact tiled softmax attention, backward pass, for gfx950.
+//
+// Follows alphabetamath.cc, "Exact tiled attention and memory-aware
+// differentiation", the Algorithm's reverse procedure: with the forward's row
+// statistics frozen (carried as LSE_i = m_i + ln l_i, so p_ij = e^{s_ij - LSE_i}),
+//   delta_i  = sum_a G_ia Y_ia
+//   gamma_ij = p_ij (sum_a G_ia V_ja - delta_i)
+//   dQ_i += c gamma_ij K_j,  dK_j += c gamma_ij Q_i,  dV_j += p_ij G_i,
+// recomputing every score block from Q, K instead of storing it (WebTuring
+// Principia, "Bellek Duvarinin Fizigi", section on backpropagation by
+// recomputation: P is rebuilt from the saved log-sum-exp).
+//
+// Three kernels, no atomics (deterministic):
+//   1. delta: one fp32 per row from the stored O and dO.
+//   2. dK/dV: a workgroup keeps 128 keys of K and V in registers (32 per wave)
+//      and streams the query tiles that may see them through LDS.  Scores are
+//      formed as S = Q K^T so every lane holds one KEY column: P and dS then
+//      feed dV^T += dO^T P and dK^T += Q^T dS straight from registers.
+//   3. dQ: a workgroup keeps 128 query rows (Q, dO, LSE, delta) in registers
+//      and streams key/value tiles through LDS, as the forward does, with
+//      dQ^T += K^T dS^T.
+// Transposed LDS copies (dO^T, Q^T, K^T) are written while staging, from the
+// same registers that hold the natural copies.
+#include "attn_device.h"
+#include "attn_internal.h"
+
+namespace eiat {
+
+// Stage ROWS consecutive rows of a [n][D] slice into LDS: a natural copy (row
+// stride NROW bytes) and/or a transposed copy (DP rows of ROWS elements, stride
+// TROW bytes).  Each task is 4 rows x 16 bytes; rows >= n read as zero.
+template <typename T, int D, int ROWS, int THREADS, int NROW, int TROW, bool NAT, bool TR>
+struct Stager {
+  static constexpr int S = Elt<T>::kBytes;
+  static constexpr int CPR = D * S / 16;
+  static constexpr int EPC = 16 / S;
+  static constexpr int TASKS = (ROWS / 4) * CPR;
+  static constexpr int PT = (TASKS + THREADS - 1) / THREADS;
+  u32x4 reg[PT][4];
+
+  __device__ inline void load(const char* base, int r0, int n, int tid) {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int task = tid + p * THREADS;
+      if (task < TASKS) {
+        const int rq = task / CPR, col = task % CPR;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + 4 * rq + i;
+          reg[p][i] = r < n ? ldg16(base + (int64_t)r * D * S + col * 16) : zero4();
+        }
+      }
+    }
+  }
+
+  __device__ inline void store(char* nat, char* tr, int tid) {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int task = tid + p * THREADS;
+      if (task < TASKS) {
+        const int rq = task / CPR, col = task % CPR;
+        if constexpr (NAT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4*>(nat + (4 * rq + i) * NROW + col * 16) = reg[p][i];
+        }
+        if constexpr (TR) store_transposed4<T>(tr + (col * EPC) * TROW + 4 * rq * S, TROW, reg[p]);
+      }
+    }
+  }
+};
+
+// Zero rows [D, DP) of a transposed tile (only when D < 32).
+template <int D, int DP, int TROW, int THREADS>
+__device__ inline void zero_pad_rows(char* tr, int tid) {
+  if constexpr (DP > D) {
+    constexpr int per_row = TROW / 16;
+    for (int idx = tid; idx < (DP - D) * per_row; idx += THREADS)
+      *reinterpret_cast<u32x4*>(tr + (D + idx / per_row) * TROW + (idx % per_row) * 16) = zero4();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1. delta_i = sum_a dO_ia O_ia
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const T* __restrict__ O,
+                                                             const T* __restrict__ dO,
+                                                             float* __restrict__ delta,
+                                                             int64_t rows) {
+  constexpr int S = Elt<T>::kBytes;
+  constexpr int CPR = D * S / 16;  // threads per row (a power of two <= 32)
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gt / CPR;
+  const int col = (int)(gt % CPR);
+  float acc = 0.0f;
+  if (row < rows) {
+    u32x4 a = ldg16(reinterpret_cast<const char*>(O) + row * D * S + col * 16);
+    u32x4 b = ldg16(reinterpret_cast<const char*>(dO) + row * D * S + col * 16);
+    if constexpr (S == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float a0, a1, b0, b1;
+        if constexpr (__is_same(T, __bf16)) {
+          a0 = __uint_as_float(a[w] << 16);
+          a1 = __uint_as_float(a[w] & 0xFFFF0000u);
+          b0 = __uint_as_float(b[w] << 16);
+          b1 = __uint_as_float(b[w] & 0xFFFF0000u);
+        } else {
+          f16x2 ah = __builtin_bit_cast(f16x2, a[w]), bh = __builtin_bit_cast(f16x2, b[w]);
+          a0 = (float)ah[0];
+          a1 = (float)ah[1];
+          b0 = (float)bh[0];
+          b1 = (float)bh[1];
+        }
+        acc = __builtin_fmaf(a0, b0, acc);
+        acc = __builtin_fmaf(a1, b1, acc);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc = __builtin_fmaf(__uint_as_float(a[w]), __uint_as_float(b[w]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && col == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK / dV: keys resident, query tiles streamed
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DkvCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BNK = 32 * kWaves;            // keys per workgroup
+  static constexpr int BMQ = D >= 128 ? 32 : 64;     // query rows per streamed tile
+  static constexpr int DP = D < 32 ? 32 : D;
+  static constexpr int S = Elt<T>::kBytes;
+  static constexpr int NROW = D * S + 16;            // Q / dO natural rows
+  static constexpr int TROW = BMQ * S + 16;          // Q^T / dO^T rows
+  static constexpr int QN = 0;
+  static constexpr int QT = QN + BMQ * NROW;
+  static constexpr int ON = QT + DP * TROW;
+  static constexpr int OT = ON + BMQ * NROW;
+  static constexpr int LS = OT + DP * TROW;          // LSE * log2(e), BMQ floats
+  static constexpr int DL = LS + BMQ * 4;            // delta, BMQ floats
+  static constexpr int BUF = DL + BMQ * 4;
+  static constexpr int NCH = D * S / 32;
+  static constexpr int NOB = DP / 32;
+  static constexpr int NQB = BMQ / 32;
+};
+
+template <typename T, int D, int MASK>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    T* __restrict__ dK, T* __restrict__ dV, int n, int bh_count, int num_ktiles, int window,
+    float qk_scale, int qmode, float scale) {
+  using C = DkvCfg<T, D>;
+  constexpr int BMQ = C::BMQ;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+  using St = Stager<T, D, BMQ, C::kThreads, C::NROW, C::TROW, true, true>;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int bh = bid % bh_count;
+  int kt = bid / bh_count;
+  // Causal: key tiles near the start are seen by the most queries; issue them first.
+  (void)num_ktiles;
+  const int k0 = kt * C::BNK;
+  const int kw0 = k0 + 32 * wave;
+  const int key = kw0 + l32;
+
+  const int64_t head = (int64_t)bh * n;
+  const char* Qh = reinterpret_cast<const char*>(Q + head * D);
+  const char* Kh = reinterpret_cast<const char*>(K + head * D);
+  const char* Vh = reinterpret_cast<const char*>(V + head * D);
+  const char* dOh = reinterpret_cast<const char*>(dO + head * D);
+  const float* LSEh = LSE + head;
+  const float* Dh = delta + head;
+
+  // This wave's 32 keys of K and V as B-operand chunks (lane: key kw0 + L%32).
+  u32x4 kf[C::NCH], vf[C::NCH];
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    kf[c] = key < n ? ldg16(Kh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
+    vf[c] = key < n ? ldg16(Vh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
+    if (qmode == 1) kf[c] ^= Elt<T>::kSign;
+  }
+
+  // Query rows that may see any key of this workgroup.
+  int qbeg = 0, qend = n;
+  if (MASK != 0) qbeg = k0;
+  if (MASK == 2) qend = (int)min((int64_t)n, (int64_t)k0 + C::BNK - 1 + window);
+  const int t_lo = qbeg / BMQ, t_hi = (qend + BMQ - 1) / BMQ;
+
+  f32x16 dk[C::NOB], dv[C::NOB];
+#pragma unroll
+  for (int ob = 0; ob < C::NOB; ++ob)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[ob][e] = 0.0f;
+      dv[ob][e] = 0.0f;
+    }
+
+  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::QT, tid);
+  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::OT, tid);
+  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::BUF + C::QT, tid);
+  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::BUF + C::OT, tid);
+
+  St sq, so;
+  float4 lreg, dreg;  // LSE * log2(e) and delta for 4 rows (threads < BMQ / 4)
+
+  auto load_tile = [&](int t) {
+    const int r0 = t * BMQ;
+    sq.load(Qh, r0, n, tid);
+    so.load(dOh, r0, n, tid);
+    if (tid < BMQ / 4) {
+      float* lr = reinterpret_cast<float*>(&lreg);
+      float* dr = reinterpret_cast<float*>(&dreg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * tid + i;
+        // rows past n contribute nothing: p = 2^(-inf) = 0
+        lr[i] = r < n ? LSEh[r] * kLog2e : INFINITY;
+        dr[i] = r < n ? Dh[r] : 0.0f;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* b = smem + buf * C::BUF;
+    sq.store(b + C::QN, b + C::QT, tid);
+    so.store(b + C::ON, b + C::OT, tid);
+    if (tid < BMQ / 4) {
+      *reinterpret_cast<float4*>(b + C::LS + 16 * tid) = lreg;
+      *reinterpret_cast<float4*>(b + C::DL + 16 * tid) = dreg;
+    }
+  };
+
+  if (t_lo < t_hi) {
+    load_tile(t_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    const bool has_next = t + 1 < t_hi;
+    if (has_next) load_tile(t + 1);
+    const int qt0 = t * BMQ;
+
+    bool empty = false;
+    if (MASK != 0) empty = qt0 + BMQ - 1 < kw0;
+    if (MASK == 2) empty = empty || (qt0 > kw0 + 31 + window - 1);
+    if (!empty) {
+      const char* b = smem + buf * C::BUF;
+      bool straddle = false;
+      if (MASK != 0) straddle = qt0 < kw0 + 31;
+      if (MASK == 2) straddle = straddle || (qt0 + BMQ - 1 - window + 1 > kw0);
+      straddle = straddle || (kw0 + 32 > n);
+
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys
+        f32x16 s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[e] = 0.0f;
+          dp[e] = 0.0f;
+        }
+        const int rq = 32 * qb + l32;
+#pragma unroll
+        for (int c = 0; c < C::NCH; ++c) {
+          u32x4 qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
+          u32x4 oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
+          if (qmode != 2) s = Elt<T>::mma(qa, kf[c], s);
+          dp = Elt<T>::mma(oa, vf[c], dp);
+        }
+        if (straddle) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int q = qt0 + 32 * qb + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (!key_allowed<MASK>(q, key, n, window)) s[e] = -INFINITY;
+          }
+        }
+        // p = 2^(s c log2 e - LSE log2 e), dS = p (dP - delta)
+        const float* ls = reinterpret_cast<const float*>(b + C::LS);
+        const float* dl = reinterpret_cast<const float*>(b + C::DL);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 l4 = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * g + 4 * h);
+          const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dvl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * g + i;
+            const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lv[i]));
+            s[e] = p;
+            dp[e] = p * (dp[e] - dvl[i]);
+          }
+        }
+        PChunks<T> pc, dsc;
+        pc.set(s);
+        dsc.set(dp);
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) {
+          const char* orow = b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S;
+          const char* qrow = b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S;
+#pragma unroll
+          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+            dv[ob] = Elt<T>::mma(keyrow_chunk<T>(orow, ci, h), pc.c[ci], dv[ob]);
+            dk[ob] = Elt<T>::mma(keyrow_chunk<T>(qrow, ci, h), dsc.c[ci], dk[ob]);
+          }
+        }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds column `key`, rows a = 32 ob + 8 g + 4 h + (0..3).
+  if (key < n) {
+    char* dkrow = reinterpret_cast<char*>(dK + (head + key) * D);
+    char* dvrow = reinterpret_cast<char*>(dV + (head + key) * D);
+#pragma unroll
+    for (int ob = 0; ob < C::NOB; ++ob)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = 32 * ob + 8 * g + 4 * h;
+        if (a0 < D) {
+          if constexpr (C::S == 2) {
+            u32x2 wk = {Elt<T>::pack2(dk[ob][4 * g] * scale, dk[ob][4 * g + 1] * scale),
+                        Elt<T>::pack2(dk[ob][4 * g + 2] * scale, dk[ob][4 * g + 3] * scale)};
+            u32x2 wv = {Elt<T>::pack2(dv[ob][4 * g], dv[ob][4 * g + 1]),
+                        Elt<T>::pack2(dv[ob][4 * g + 2], dv[ob][4 * g + 3])};
+            *reinterpret_cast<u32x2*>(dkrow + a0 * C::S) = wk;
+            *reinterpret_cast<u32x2*>(dvrow + a0 * C::S) = wv;
+          } else {
+            f32x4 wk = {dk[ob][4 * g] * scale, dk[ob][4 * g + 1] * scale,
+                        dk[ob][4 * g + 2] * scale, dk[ob][4 * g + 3] * scale};
+            f32x4 wv = {dv[ob][4 * g], dv[ob][4 * g + 1], dv[ob][4 * g + 2], dv[ob][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(dkrow + a0 * C::S) = wk;
+            *reinterpret_cast<f32x4*>(dvrow + a0 * C::S) = wv;
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ: queries resident, key/value tiles streamed
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BM = 32 * kWaves;
+  static constexpr int S = Elt<T>::kBytes;
+  static constexpr int BN = (S == 4 && D >= 128) ? 32 : 64;  // keys per streamed tile
+  static constexpr int DP = D < 32 ? 32 : D;
+  static constexpr int NROW = D * S + 16;   // K, V natural rows
+  static constexpr int TROW = BN * S + 16;  // K^T rows
+  static constexpr int KN = 0;
+  static constexpr int KT = KN + BN * NROW;
+  static constexpr int VN = KT + DP * TROW;
+  static constexpr int BUF = VN + BN * NROW;
+  static constexpr int NCH = D * S / 32;
+  static constexpr int NOB = DP / 32;
+  static constexpr int NSB = BN / 32;
+};
+
+template <typename T, int D, int MASK>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    T* __restrict__ dQ, int n, int bh_count, int num_qtiles, int window, float qk_scale,
+    int qmode, float scale) {
+  using C = DqCfg<T, D>;
+  constexpr int BN = C::BN;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+  using StK = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, true>;
+  using StV = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, false>;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int bh = bid % bh_count;
+  int qt = bid / bh_count;
+  if (MASK != 0) qt = num_qtiles - 1 - qt;
+  const int q0 = qt * C::BM;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + l32;
+
+  const int64_t head = (int64_t)bh * n;
+  const char* Qh = reinterpret_cast<const char*>(Q + head * D);
+  const char* Kh = reinterpret_cast<const char*>(K + head * D);
+  const char* Vh = reinterpret_cast<const char*>(V + head * D);
+  const char* dOh = reinterpret_cast<const char*>(dO + head * D);
+
+  u32x4 qf[C::NCH], of[C::NCH];
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    qf[c] = qrow < n ? ldg16(Qh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
+    of[c] = qrow < n ? ldg16(dOh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
+    if (qmode == 1) qf[c] ^= Elt<T>::kSign;
+  }
+  const float lse2 = qrow < n ? LSE[head + qrow] * kLog2e : INFINITY;
+  const float dlt = qrow < n ? delta[head + qrow] : 0.0f;
+
+  int kend = n;
+  if (MASK != 0) kend = min(n, q0 + C::BM);
+  int kbeg = 0;
+  if (MASK == 2) kbeg = max(0, q0 - window + 1);
+  const int t_lo = kbeg / BN, t_hi = (kend + BN - 1) / BN;
+
+  f32x16 dq[C::NOB];
+#pragma unroll
+  for (int ob = 0; ob < C::NOB; ++ob)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[ob][e] = 0.0f;
+
+  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::KT, tid);
+  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::BUF + C::KT, tid);
+
+  StK sk;
+  StV sv;
+  auto load_tile = [&](int t) {
+    sk.load(Kh, t * BN, n, tid);
+    sv.load(Vh, t * BN, n, tid);
+  };
+  auto store_tile = [&](int buf) {
+    char* b = smem + buf * C::BUF;
+    sk.store(b + C::KN, b + C::KT, tid);
+    sv.store(b + C::VN, nullptr, tid);
+  };
+
+  load_tile(t_lo);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    const bool has_next = t + 1 < t_hi;
+    if (has_next) load_tile(t + 1);
+    const int j0 = t * BN;
+    bool empty = false;
+    if (MASK != 0) empty = j0 > qw0 + 31;
+    if (MASK == 2) empty = empty || (j0 + BN - 1 < qw0 - window + 1);
+    if (!empty) {
+      const char* b = smem + buf * C::BUF;
+      bool straddle = j0 + BN > n;
+      if (MASK != 0) straddle = straddle || (j0 + BN - 1 > qw0);
+      if (MASK == 2) straddle = straddle || (j0 < qw0 + 31 - window + 1);
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        // S^T = K Q^T and dP^T = V dO^T: lane holds one query row, 16 keys per half
+        f32x16 s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[e] = 0.0f;
+          dp[e] = 0.0f;
+        }
+        const int rk = 32 * sb + l32;
+#pragma unroll
+        for (int c = 0; c < C::NCH; ++c) {
+          u32x4 ka = *reinterpret_cast<const u32x4*>(b + C::KN + rk * C::NROW + 32 * c + 16 * h);
+          u32x4 va = *reinterpret_cast<const u32x4*>(b + C::VN + rk * C::NROW + 32 * c + 16 * h);
+          if (qmode != 2) s = Elt<T>::mma(ka, qf[c], s);
+          dp = Elt<T>::mma(va, of[c], dp);
+        }
+        if (straddle) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (!key_allowed<MASK>(qrow, j, n, window)) s[e] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
+          dp[e] = p * (dp[e] - dlt);
+        }
+        PChunks<T> dsc;
+        dsc.set(dp);
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) {
+          const char* krow = b + C::KT + (32 * ob + l32) * C::TROW + 32 * sb * C::S;
+#pragma unroll
+          for (int ci = 0; ci < PChunks<T>::kCount; ++ci)
+            dq[ob] = Elt<T>::mma(keyrow_chunk<T>(krow, ci, h), dsc.c[ci], dq[ob]);
+        }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow < n) {
+    char* dqrow = reinterpret_cast<char*>(dQ + (head + qrow) * D);
+#pragma unroll
+    for (int ob = 0; ob < C::NOB; ++ob)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = 32 * ob + 8 * g + 4 * h;
+        if (a0 < D) {
+          if constexpr (C::S == 2) {
+            u32x2 w = {Elt<T>::pack2(dq[ob][4 * g] * scale, dq[ob][4 * g + 1] * scale),
+                       Elt<T>::pack2(dq[ob][4 * g + 2] * scale, dq[ob][4 * g + 3] * scale)};
+            *reinterpret_cast<u32x2*>(dqrow + a0 * C::S) = w;
+          } else {
+            f32x4 w = {dq[ob][4 * g] * scale, dq[ob][4 * g + 1] * scale,
+                       dq[ob][4 * g + 2] * scale, dq[ob][4 * g + 3] * scale};
+            *reinterpret_cast<f32x4*>(dqrow + a0 * C::S) = w;
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+template <typename T, int D, int MASK>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  const int64_t rows = a.bh * a.n;
+  {
+    constexpr int CPR = D * Elt<T>::kBytes / 16;
+    const int64_t blocks = (rows * CPR + 255) / 256;
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dout),
+                       a.delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    using C = DkvCfg<T, D>;
+    const int num_ktiles = (int)((a.n + C::BNK - 1) / C::BNK);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, MASK>), dim3((unsigned)(num_ktiles * a.bh)),
+                       dim3(C::kThreads), 0, a.stream, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dk),
+                       static_cast<T*>(a.dv), (int)a.n, (int)a.bh, num_ktiles, (int)a.window,
+                       a.qk_scale, a.qmode, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    using C = DqCfg<T, D>;
+    const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK>), dim3((unsigned)(num_qtiles * a.bh)),
+                       dim3(C::kThreads), 0, a.stream, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dq),
+                       (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
+                       a.scale);
+    return hipGetLastError();
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_d(const BwdArgs& a) {
+  switch (a.mask) {
+    case 0: return launch_bwd_t<T, D, 0>(a);
+    case 1: return launch_bwd_t<T, D, 1>(a);
+    default: return launch_bwd_t<T, D, 2>(a);
+  }
+}
+
+template <typename T>
+static hipError_t launch_bwd_dt(const BwdArgs& a) {
+  switch (a.d) {
+    case 16: return launch_bwd_d<T, 16>(a);
+    case 64: return launch_bwd_d<T, 64>(a);
+    default: return launch_bwd_d<T, 128>(a);
+  }
+}
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  switch (a.dtype) {
+    case 0: return launch_bwd_dt<float>(a);
+    case 1: return launch_bwd_dt<_Float16>(a);
+    default: return launch_bwd_dt<__bf16>(a);
+  }
+}
+
+}  // namespace eiat

@@ -1,0 +1,168 @@
+// attn_device.h -- device-side building blocks shared by the forward and
+// backward attention kernels for gfx950 (CDNA4, wave64).
+//
+// Matrix products use the 32x32 MFMA shapes with fp32 accumulation:
+//   16-bit inputs: v_mfma_f32_32x32x16_{bf16,f16}; float32: v_mfma_f32_32x32x2_f32.
+// Operand convention used throughout ("one 16-byte chunk per lane"): for a
+// product C[32][32] += A[32][k] * B[k][32], lane L supplies row (L % 32) of A
+// and column (L % 32) of B; the contraction indices covered by one chunk are
+// split between the two half-waves (h = L / 32).  Because A and B assign the
+// same contraction index to the same (half, element) slot, any consistent
+// assignment of indices to slots gives the same product; the kernels choose the
+// assignment that matches where the data already sits.
+//
+// Accumulator layout of a 32x32 fp32 block (16 values per lane):
+//   element e of lane L holds C[8*(e/4) + 4*h + (e%4)][L % 32].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eiat {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element traits: one MFMA step over a 16-byte chunk per lane, and fp32 -> T packing.
+template <typename T>
+struct Elt;
+
+template <>
+struct Elt<__bf16> {
+  static constexpr int kBytes = 2;
+  static constexpr uint32_t kSign = 0x80008000u;
+  // 16 contraction indices: elements 0..7 of the chunk in each half-wave.
+  __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32).
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+};
+
+template <>
+struct Elt<_Float16> {
+  static constexpr int kBytes = 2;
+  static constexpr uint32_t kSign = 0x80008000u;
+  __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+};
+
+template <>
+struct Elt<float> {
+  static constexpr int kBytes = 4;
+  static constexpr uint32_t kSign = 0x80000000u;
+  // Four K=2 steps: element e of the chunk in half-wave h is one contraction index.
+  __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c, 0,
+                                               0, 0);
+    return c;
+  }
+};
+
+// Probability operand: the 16 fp32 values of one 32-key accumulator block (keys
+// 8*(e/4) + 4*h + (e%4) of column L % 32) as MFMA chunks over those keys.
+// 16-bit types: chunk s (0, 1) holds elements 8s..8s+7 -> keys 16s + 8*(i/4) + 4h + (i%4).
+// float32: chunk g (0..3) holds elements 4g..4g+3     -> keys 8g + 4h + i.
+template <typename T>
+struct PChunks {
+  static constexpr int kCount = (Elt<T>::kBytes == 2) ? 2 : 4;
+  u32x4 c[kCount];
+  __device__ inline void set(const f32x16& p) {
+    if constexpr (Elt<T>::kBytes == 2) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) c[s][w] = Elt<T>::pack2(p[8 * s + 2 * w], p[8 * s + 2 * w + 1]);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) c[g][w] = __float_as_uint(p[4 * g + w]);
+    }
+  }
+};
+
+// Load the "transposed" operand matching PChunks from an LDS row that stores 32
+// consecutive keys of one output row (row-major over keys, element type T):
+// chunk index ci covers the same keys as PChunks<T>::c[ci] for half-wave h.
+template <typename T>
+__device__ inline u32x4 keyrow_chunk(const char* row32, int ci, int h) {
+  if constexpr (Elt<T>::kBytes == 2) {
+    // keys 16ci + 4h + 0..3 and 16ci + 8 + 4h + 0..3 (8 bytes each)
+    u32x2 lo = *reinterpret_cast<const u32x2*>(row32 + (16 * ci + 4 * h) * 2);
+    u32x2 hi = *reinterpret_cast<const u32x2*>(row32 + (16 * ci + 8 + 4 * h) * 2);
+    u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
+    return r;
+  } else {
+    // keys 8ci + 4h + 0..3 (16 bytes)
+    return *reinterpret_cast<const u32x4*>(row32 + (8 * ci + 4 * h) * 4);
+  }
+}
+
+__device__ inline float wave_swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ inline u32x4 zero4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+__device__ inline u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Transpose four 16-byte rows (4 keys x E elements of T) into E rows of 4 keys
+// and write them to LDS: row e of the output goes to dst + e * row_stride.
+template <typename T>
+__device__ inline void store_transposed4(char* dst, int row_stride, const u32x4 (&r)[4]) {
+  if constexpr (Elt<T>::kBytes == 2) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // column 2p: low halves; column 2p + 1: high halves
+      u32x2 even = {(r[0][p] & 0xFFFFu) | (r[1][p] << 16), (r[2][p] & 0xFFFFu) | (r[3][p] << 16)};
+      u32x2 odd = {(r[0][p] >> 16) | (r[1][p] & 0xFFFF0000u),
+                   (r[2][p] >> 16) | (r[3][p] & 0xFFFF0000u)};
+      *reinterpret_cast<u32x2*>(dst + (2 * p) * row_stride) = even;
+      *reinterpret_cast<u32x2*>(dst + (2 * p + 1) * row_stride) = odd;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u32x4 col = {r[0][e], r[1][e], r[2][e], r[3][e]};
+      *reinterpret_cast<u32x4*>(dst + e * row_stride) = col;
+    }
+  }
+}
+
+// Allowed-key membership for the three mask kinds (0 none, 1 causal, 2 window).
+template <int MASK>
+__device__ inline bool key_allowed(int q, int j, int n, int window) {
+  bool ok = j < n;
+  if constexpr (MASK != 0) ok = ok && (j <= q);
+  if constexpr (MASK == 2) ok = ok && (j >= q - window + 1);
+  return ok;
+}
+
+}  // namespace eiat

@@ -1,0 +1,54 @@
+// attn_internal.h -- host-side launch interface between the C ABI entry points
+// (attn_api.hip) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eiat {
+
+// Arguments of one forward launch, already validated by the entry point.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t bh;        // B * H
+  int64_t n;
+  int d;             // == dv
+  int dtype;         // 0 f32, 1 f16, 2 bf16
+  int mask;          // 0 none, 1 causal, 2 window
+  int64_t window;    // allowed keys per row (mask 2), clamped to n
+  float qk_scale;    // |c| * log2(e), or 1 when c == 0
+  int qmode;         // 0: c > 0, 1: c < 0 (Q negated), 2: c == 0 (Q taken as 0)
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;      // workspace, bh * n floats
+  int64_t bh;
+  int64_t n;
+  int d;
+  int dtype;
+  int mask;
+  int64_t window;
+  float qk_scale;    // as FwdArgs
+  int qmode;
+  float scale;       // c itself (multiplies dQ and dK)
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+
+}  // namespace eiat

@@ -1,0 +1,134 @@
+/*
+ * eiat_attn.h -- C ABI of the exact IO-aware tiled attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is masked row-softmax attention as defined on alphabetamath.cc,
+ * "Exact tiled attention and memory-aware differentiation" (Definition "Stable
+ * summary of an attention key block"; Theorem "Tiled attention and its
+ * recomputed reverse pass are exact"): for every batch b, head h and query row i
+ *
+ *     s_ij = c * sum_r Q_ir K_jr                (j in the allowed set A_i)
+ *     O_i  = sum_{j in A_i} e^{s_ij} V_j / sum_{j in A_i} e^{s_ij}
+ *     LSE_i = ln sum_{j in A_i} e^{s_ij}   (= m_i + ln l_i of the summary)
+ *
+ * and its reverse (the Algorithm "Exact tiled softmax attention with
+ * block-recomputed vector-Jacobian products", reverse procedure): given the
+ * upstream gradient dO = G, the gradients dQ, dK, dV of Phi = sum G * O.
+ *
+ * Allowed-key sets, 0-based rows i and keys j:
+ *     EIAT_MASK_NONE    every key, 0 <= j < n
+ *     EIAT_MASK_CAUSAL  j <= i (the diagonal is allowed)
+ *     EIAT_MASK_WINDOW  max(0, i - window + 1) <= j <= i; window >= 1 counts the
+ *                       allowed keys including the diagonal (window >= n is causal)
+ * Every row therefore has a nonempty allowed set.
+ *
+ * Layout.  All tensors are contiguous, row-major, head-major:
+ *     q, k, dq, dk : [B][H][n][d]       elements of `dtype`
+ *     v, o, do, dv : [B][H][n][dv]      elements of `dtype`
+ *     lse          : [B][H][n]          float32, natural logarithm
+ * Pointers are device pointers (memory the caller allocated on the current
+ * HIP device), 16-byte aligned.  The library never allocates or frees memory;
+ * every buffer is owned by the caller.  Outputs must not overlap inputs.
+ *
+ * Execution.  Calls enqueue kernels on `stream` (a hipStream_t; NULL is the
+ * null stream) and return without waiting.  Results are deterministic: the
+ * same inputs give bitwise-identical outputs (no atomics).
+ *
+ * Errors.  The return code is the only error channel; nothing is thrown.
+ * Argument errors are detected on the host before any HIP call, so they can be
+ * tested without a GPU.  attn_last_error() gives a thread-local message for
+ * the last non-OK return of the calling thread.
+ *
+ * Supported kernels: dtype F32, F16 or BF16 (fp32 accumulation in every case),
+ * d == dv in {16, 64, 128}.  Scores c * q_i . k_j must be finite in float32.
+ */
+#ifndef EIAT_ATTN_H
+#define EIAT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EIAT_ABI_VERSION 1
+
+/* Symbols of the shared library (built with hidden default visibility). */
+#if defined(__GNUC__)
+#define EIAT_API __attribute__((visibility("default")))
+#else
+#define EIAT_API
+#endif
+
+typedef enum {
+    EIAT_OK = 0,
+    EIAT_ERR_INVALID_ARG = 1, /* a null pointer, a negative size, an unknown enum, window < 1,
+                                 a misaligned pointer or a too-small workspace */
+    EIAT_ERR_UNSUPPORTED = 2, /* valid mathematics with no kernel here (d or dv not in
+                                 {16, 64, 128}, d != dv, sizes beyond int32 row indexing) */
+    EIAT_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} eiat_status;
+
+typedef enum { EIAT_F32 = 0, EIAT_F16 = 1, EIAT_BF16 = 2 } eiat_dtype;
+
+typedef enum { EIAT_MASK_NONE = 0, EIAT_MASK_CAUSAL = 1, EIAT_MASK_WINDOW = 2 } eiat_mask;
+
+/*
+ * Forward pass: the Algorithm's forward procedure (load a query tile, stream
+ * key/value tiles past it, keep the running max m, shifted normaliser l and
+ * weighted value sum z, merged with the e^{m - m'} rescale; skip key tiles with
+ * no allowed key).  Writes O (in `dtype`) and LSE = m + ln l (float32) only;
+ * no n x n array is formed.
+ *
+ *   q, k, v   inputs as laid out above
+ *   o, lse    outputs; lse is required (the backward consumes it)
+ *   B, H, n   batch, heads, sequence length (>= 0; zero-sized calls do nothing)
+ *   d, dv     head dims of q/k and of v/o
+ *   dtype     element type of q, k, v and o
+ *   scale     c, any finite float (c = 0 gives the mean of the allowed values)
+ *   mask, window  allowed-key sets as above; window is read only for EIAT_MASK_WINDOW
+ *   stream    hipStream_t or NULL
+ */
+EIAT_API eiat_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                     int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale, int mask,
+                     int64_t window, void *stream);
+
+/* Bytes of device workspace attn_bwd needs: the per-row delta_i, B*H*n float32. */
+EIAT_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n);
+
+/*
+ * Backward pass: the Algorithm's reverse procedure with the forward's maxima
+ * and normalisers frozen (carried here as lse).  First delta_i = sum_a dO_ia O_ia
+ * into `workspace`, then one kernel that holds a key/value tile and streams the
+ * query tiles that may see it (dK, dV), then one that holds a query tile and
+ * streams key/value tiles (dQ).  Each recomputes its score blocks from q, k and
+ * lse: p_ij = e^{s_ij - LSE_i}, gamma_ij = p_ij (dO_i . V_j - delta_i),
+ * dQ_i = c sum_j gamma_ij K_j, dK_j = c sum_i gamma_ij Q_i, dV_j = sum_i p_ij dO_i.
+ *
+ *   q, k, v, o, lse   the forward's inputs and outputs (o, lse from attn_fwd)
+ *   dout              upstream gradient dO, [B][H][n][dv]
+ *   dq, dk, dvv       outputs in `dtype`
+ *   workspace         device memory of at least attn_bwd_workspace_bytes(B, H, n)
+ *   workspace_bytes   its size
+ * Other arguments as for attn_fwd and with the same values.
+ */
+EIAT_API eiat_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                     const float *lse, void *dq, void *dk, void *dvv, void *workspace,
+                     size_t workspace_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
+                     int64_t dv, int dtype, float scale, int mask, int64_t window, void *stream);
+
+/* Static string naming a status code. */
+EIAT_API const char *attn_status_string(int status);
+
+/* Thread-local detail of the calling thread's last non-OK return ("" if none). */
+EIAT_API const char *attn_last_error(void);
+
+/* EIAT_ABI_VERSION of the built library. */
+EIAT_API int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EIAT_ATTN_H */

@@ -1,0 +1,78 @@
+"""Shared test utilities: tolerances, row sampling, and GPU-vs-oracle comparison.
+
+Tolerances (the bar each GPU result must meet against the fp64 oracle):
+  float32 inputs             : max |err| <= 1e-5 on O and LSE
+  bf16 / fp16 inputs, fp32 acc: max |err| <= 2e-2 on O, <= 1e-3 on LSE,
+                               and dQ, dK, dV within 5e-2 normwise-relative error
+                               (max |err| / max |oracle| over each (b, h) slice).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+TOL_F32 = 1e-5
+TOL_O_16 = 2e-2
+TOL_LSE_16 = 1e-3
+TOL_GRAD_16 = 5e-2
+# float32 gradients: an absolute bound scaled by the slice's largest value
+TOL_GRAD_F32 = 1e-5
+
+
+def announce(msg: str):
+    """Name the case on stderr before a GPU step, flushed, so a crash names it."""
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of fp16/bf16/fp32 values to float64 on the CPU."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def sample_rows(n: int, count: int, seed: int, must=()) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = set(int(r) for r in must if 0 <= r < n)
+    if count >= n:
+        return np.arange(n)
+    while len(rows) < count:
+        rows.add(int(rng.integers(0, n)))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def fwd_tolerances(dtype: torch.dtype):
+    if dtype == torch.float32:
+        return TOL_F32, TOL_F32
+    return TOL_O_16, TOL_LSE_16
+
+
+def check_fwd(o_gpu, lse_gpu, y_ref, lse_ref, dtype, what=""):
+    """o_gpu/lse_gpu: numpy float64 of the GPU outputs at the compared rows."""
+    tol_o, tol_l = fwd_tolerances(dtype)
+    err_o = float(np.max(np.abs(o_gpu - y_ref))) if o_gpu.size else 0.0
+    err_l = float(np.max(np.abs(lse_gpu - lse_ref))) if lse_gpu.size else 0.0
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), f"{what}: non-finite"
+    assert err_o <= tol_o, f"{what}: O max abs err {err_o:.3g} > {tol_o}"
+    assert err_l <= tol_l, f"{what}: LSE max abs err {err_l:.3g} > {tol_l}"
+    return err_o, err_l
+
+
+def check_grad(g_gpu, g_ref, dtype, what=""):
+    """Per (b, h) slice: max |err| / max |ref| (16-bit) or max |err| (fp32, scaled)."""
+    assert np.all(np.isfinite(g_gpu)), f"{what}: non-finite gradient"
+    g_gpu = g_gpu.reshape(-1, *g_gpu.shape[-2:])
+    g_ref = g_ref.reshape(-1, *g_ref.shape[-2:])
+    worst = 0.0
+    for s in range(g_gpu.shape[0]):
+        err = float(np.max(np.abs(g_gpu[s] - g_ref[s])))
+        ref = max(float(np.max(np.abs(g_ref[s]))), 1e-30)
+        if dtype == torch.float32:
+            bound = TOL_GRAD_F32 * max(1.0, ref)
+            assert err <= bound, f"{what}[{s}]: max abs err {err:.3g} > {bound:.3g}"
+            worst = max(worst, err / max(1.0, ref))
+        else:
+            rel = err / ref
+            assert rel <= TOL_GRAD_16, f"{what}[{s}]: normwise rel err {rel:.3g} > {TOL_GRAD_16}"
+            worst = max(worst, rel)
+    return worst

@@ -1,0 +1,97 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+
+import pytest
+
+from exact_io_aware_tiled_amd import attn as A
+
+F = 16  # a fake, 16-byte aligned, non-null "device" address; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return A.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = A.header_functions()
+    assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+                          "attn_status_string", "attn_last_error", "attn_abi_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.attn_abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert lib.attn_status_string(0) == b"EIAT_OK"
+    assert lib.attn_status_string(1) == b"EIAT_ERR_INVALID_ARG"
+    assert lib.attn_status_string(2) == b"EIAT_ERR_UNSUPPORTED"
+    assert lib.attn_status_string(3) == b"EIAT_ERR_HIP"
+    assert lib.attn_status_string(99) == b"EIAT_UNKNOWN_STATUS"
+
+
+def test_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(4, 16, 8192) == 4 * 16 * 8192 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 16, 8192) == 0
+
+
+def fwd(lib, q=F, k=F * 2**20, v=F * 2**21, o=F * 2**22, lse=F * 2**23, B=1, H=1, n=64, d=64,
+        dv=64, dtype=2, scale=0.125, mask=1, window=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, n, d, dv, dtype, scale, mask, window, None)
+
+
+def bwd(lib, ws_bytes=None, **kw):
+    args = dict(q=F, k=F * 2**20, v=F * 2**21, o=F * 2**22, do=F * 2**23, lse=F * 2**24,
+                dq=F * 2**25, dk=F * 2**26, dv=F * 2**27, ws=F * 2**28, B=1, H=1, n=64, d=64,
+                dv_=64, dtype=2, scale=0.125, mask=1, window=0)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = args["B"] * args["H"] * args["n"] * 4
+    return lib.attn_bwd(args["q"], args["k"], args["v"], args["o"], args["do"], args["lse"],
+                        args["dq"], args["dk"], args["dv"], args["ws"], ws_bytes, args["B"],
+                        args["H"], args["n"], args["d"], args["dv_"], args["dtype"],
+                        args["scale"], args["mask"], args["window"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(lse=0), 1), (dict(B=-1), 1), (dict(n=-5), 1), (dict(d=0), 1),
+    (dict(dtype=7), 1), (dict(mask=3), 1), (dict(mask=2, window=0), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1), (dict(q=F + 2), 1),
+    (dict(o=F), 1),  # output overlaps q
+    (dict(d=32, dv=32), 2), (dict(d=64, dv=128), 2), (dict(d=256, dv=256), 2),
+    (dict(scale=3e38), 1),  # c * log2(e) overflows float32
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert lib.attn_last_error() != b""
+
+
+def test_fwd_empty_is_ok_without_gpu(lib):
+    # nothing to do: returns before touching pointers or the GPU
+    assert fwd(lib, n=0, q=0, k=0, v=0, o=0, lse=0) == 0
+    assert fwd(lib, B=0) == 0
+    assert lib.attn_last_error() == b""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=0), 1), (dict(do=0), 1), (dict(dv_=16), 2), (dict(mask=2, window=-3), 1),
+    (dict(dq=F), 1),  # overlaps q
+    (dict(dk=F * 2**25), 1),  # overlaps dq
+    (dict(lse=F * 2**24 + 4), 1),  # misaligned
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_bwd_small_workspace(lib):
+    assert bwd(lib, ws_bytes=64 * 4 - 1) == 1
+    assert b"workspace" in lib.attn_last_error()
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.attn_fwd(q, q, q)
