@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that is
+already resident in HBM: the forward (attn_fwd: O and LSE) followed by the
+three steps of the backward (delta, dK/dV, dQ, called through attn_bwd_stage
+so each kernel can be timed on its own).  Default workload: batch 1, 32 heads,
+n = 4096, d = v = 64, bf16, causal, c = 1/8.
+
+Prints ONE JSON line on stdout.  `value` is whole-step algorithmic TFLOP/s with
+the FLOP convention: forward 4 d per allowed (query, key) pair (two products
+of 2 d), backward 2.5 x forward.  `roofline` is for the kernel with the largest
+share of the step time, from HIP events recorded around every launch in the
+timed region, against the MI355X dense bf16/fp16 MFMA peak.  `cpu_baseline`
+times the fp64 CPU oracle (the test reference, never tuned) on whole heads of
+the same workload within a bounded time budget.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd/bwd attention TFLOP/s, n=4096 d=64 bf16 causal; % of MFMA peak"
+# MI355X published dense peaks (TFLOP/s): bf16 / fp16 MFMA, fp32 MFMA
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def allowed_pairs(n: int, mask: str, window: int) -> int:
+    """Number of allowed (query, key) pairs of one head."""
+    if mask == "none":
+        return n * n
+    if mask == "causal":
+        return n * (n + 1) // 2
+    w = min(window, n)
+    return w * (w + 1) // 2 + (n - w) * w
+
+
+def convention_pairs(n: int, mask: str, window: int) -> float:
+    """Pairs used by the headline FLOP convention: n^2 / 2 for causal, as quoted."""
+    if mask == "causal":
+        return n * n / 2.0
+    return float(allowed_pairs(n, mask, window))
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_io_aware_tiled_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """Counter-derived HBM bytes per launch, if taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get("kernels", {}).get(kernel)
+    if not entry or data.get("sources_sha") != sources_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle (fwd + VJP) on whole heads of the workload until budget_s."""
+    import oracle
+    from exact_io_aware_tiled_amd.inputs import make_inputs
+
+    inp = make_inputs(w, with_grad=True)
+    flat = {x: inp[x].reshape(-1, w.n, inp[x].shape[-1]) for x in ("q", "k", "v", "do")}
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    per_head = 4.0 * w.d * convention_pairs(w.n, w.mask, w.window) * 3.5  # fwd + 2.5 x fwd
+    heads, t_total = 0, 0.0
+    for h in range(flat["q"].shape[0]):
+        args = [f64(flat[x][h]) for x in ("q", "k", "v", "do")]
+        t0 = time.perf_counter()
+        oracle.bwd(*args, w.c, w.mask, w.window)  # dense forward + analytic VJP
+        t_total += time.perf_counter() - t0
+        heads += 1
+        if t_total >= budget_s:
+            break
+    total_heads = flat["q"].shape[0]
+    return {
+        "value": per_head * heads / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 dense oracle, forward + VJP, {heads} of {total_heads} heads of the "
+                   f"same workload (n={w.n}, d={w.d}, {w.mask}); {t_total:.2f} s; "
+                   f"full-workload time at this rate {t_total * total_heads / heads:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="page_d64")
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline (0 disables)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log(f"bench.py: --gpus {args.gpus} (WORLD_SIZE {world}) requested, but this build runs "
+            "on exactly one GPU: the attention path has no multi-GPU code. Run with --gpus 1.")
+        sys.exit(2)
+
+    import torch
+
+    from exact_io_aware_tiled_amd import attn
+    from exact_io_aware_tiled_amd.inputs import DTYPES, WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = attn.load_library()
+
+    inp = make_inputs(w, with_grad=True, device=dev)
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    B, H, n, d, dv = w.B, w.H, w.n, w.d, w.dv
+    dt = DTYPES[w.dtype]
+    o = torch.empty(B, H, n, dv, dtype=dt, device=dev)
+    lse = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    dq, dk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = max(attn.attn_bwd_workspace_bytes(B, H, n), 16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = attn._stream_handle(stream)
+    dcode, mcode = attn.DTYPE_CODES[dt], attn.MASK_CODES[w.mask]
+    c = float(w.c)
+
+    def fwd():
+        s = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         B, H, n, d, dv, dcode, c, mcode, w.window, sh)
+        if s:
+            raise attn.AttnError(s, lib.attn_last_error().decode())
+
+    def bwd_stage(stage):
+        s = lib.attn_bwd_stage(stage, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dvv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, n, d, dv, dcode, c,
+                               mcode, w.window, sh)
+        if s:
+            raise attn.AttnError(s, lib.attn_last_error().decode())
+
+    kernels = [("attn_fwd", fwd)]
+    if not args.fwd_only:
+        kernels += [("bwd_delta", lambda: bwd_stage(0)), ("bwd_dkdv", lambda: bwd_stage(1)),
+                    ("bwd_dq", lambda: bwd_stage(2))]
+
+    def step(evs=None):
+        for i, (_, fn) in enumerate(kernels):
+            if evs is not None:
+                evs[i].record(stream)
+            fn()
+        if evs is not None:
+            evs[len(kernels)].record(stream)
+
+    log(f"bench: workload {w}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+              for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    kern_ms = {name: sum(events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)) / K
+               for i, (name, _) in enumerate(kernels)}
+    log("bench: kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in kern_ms.items()}))
+
+    bh = B * H
+    pairs = allowed_pairs(n, w.mask, w.window) * bh
+    conv_fwd = 4.0 * d * convention_pairs(n, w.mask, w.window) * bh
+    conv_bwd = 2.5 * conv_fwd
+    step_flops = conv_fwd + (0.0 if args.fwd_only else conv_bwd)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    # algorithmic work per launch of each kernel
+    e = 4 if w.dtype == "f32" else 2
+    work = {
+        "attn_fwd": ("mfma", 4.0 * d * pairs),      # S and P V
+        "bwd_dkdv": ("mfma", 8.0 * d * pairs),      # S, dP, dV, dK
+        "bwd_dq": ("mfma", 6.0 * d * pairs),        # S, dP, dQ
+        "bwd_delta": ("hbm", float(bh * n * (2 * dv * e + 4))),  # read O, dO; write delta
+    }
+    dom = max(kern_ms, key=kern_ms.get)
+    bound, amount = work[dom]
+    if bound == "mfma":
+        achieved = amount / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        achieved = amount / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(dom)
+
+    per_kernel = {}
+    for name, ms in kern_ms.items():
+        b_, amt = work[name]
+        rate = amt / (ms * 1e-3) / (1e12 if b_ == "mfma" else 1e9)
+        per_kernel[name] = {"ms": round(ms, 4), "bound": b_,
+                            ("tflops" if b_ == "mfma" else "gbs"): round(rate, 2)}
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration {nbytes} bytes read, {nbytes} bytes written")
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    fwd_ms = kern_ms["attn_fwd"]
+    bwd_ms = sum(v_ for k_, v_ in kern_ms.items() if k_ != "attn_fwd")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": f"{w.name}: B={B} H={H} n={n} d=v={d} {w.dtype} {w.mask}"
+                               + ("" if args.fwd_only else ", forward + backward"),
+                   "global_batch": B, "seq_len": n, "heads": H, "head_dim": d,
+                   "mask": w.mask, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "fwd_tflops": round(conv_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": None if args.fwd_only else round(conv_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -59,6 +59,8 @@ def load_library():
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                              i64, i64, i64, c_int, c_float, c_int, i64, vp]
     lib.attn_bwd.restype = c_int
+    lib.attn_bwd_stage.argtypes = [c_int] + lib.attn_bwd.argtypes
+    lib.attn_bwd_stage.restype = c_int
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [c_int]
@@ -119,8 +121,13 @@ def attn_bwd_workspace_bytes(B: int, H: int, n: int) -> int:
 
 
 def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "causal",
-             window: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV of sum(dO * O) given the forward's O and LSE."""
+             window: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None,
+             stage: Optional[int] = None):
+    """dQ, dK, dV of sum(dO * O) given the forward's O and LSE.
+
+    stage=None runs attn_bwd (all steps); stage 0, 1 or 2 runs attn_bwd_stage
+    (delta into `workspace`; dK and dV; dQ) -- pass the same workspace to all.
+    """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do)):
         _require(t, name)
@@ -133,9 +140,12 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "ca
     ws_bytes = attn_bwd_workspace_bytes(B, H, n)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H,
-                        n, d, dvd, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask],
-                        int(window), _stream_handle(stream)))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), B, H, n, d, dvd, DTYPE_CODES[q.dtype],
+            float(scale), MASK_CODES[mask], int(window), _stream_handle(stream))
+    if stage is None:
+        _check(lib.attn_bwd(*args))
+    else:
+        _check(lib.attn_bwd_stage(int(stage), *args))
     return dq, dk, dv

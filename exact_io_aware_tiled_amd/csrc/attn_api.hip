@@ -131,10 +131,11 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n) {
   return (size_t)B * (size_t)H * (size_t)n * sizeof(float);
 }
 
-eiat_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                     const float* lse, void* dq, void* dk, void* dvv, void* workspace,
-                     size_t workspace_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
-                     int64_t dv, int dtype, float scale, int mask, int64_t window, void* stream) {
+static eiat_status bwd_impl(int stages, const void* q, const void* k, const void* v,
+                            const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                            void* dvv, void* workspace, size_t workspace_bytes, int64_t B,
+                            int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale,
+                            int mask, int64_t window, void* stream) {
   bool empty = false;
   float qk_scale = 1.0f;
   int qmode = 0;
@@ -187,10 +188,29 @@ eiat_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   a.qk_scale = qk_scale;
   a.qmode = qmode;
   a.scale = scale;
+  a.stages = stages;
   a.stream = static_cast<hipStream_t>(stream);
   hipError_t e = eiat::launch_bwd(a);
   if (e != hipSuccess) return fail(EIAT_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+eiat_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dvv, void* workspace,
+                     size_t workspace_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
+                     int64_t dv, int dtype, float scale, int mask, int64_t window, void* stream) {
+  return bwd_impl(7, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H, n, d,
+                  dv, dtype, scale, mask, window, stream);
+}
+
+eiat_status attn_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dvv,
+                           void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t n, int64_t d, int64_t dv, int dtype, float scale, int mask,
+                           int64_t window, void* stream) {
+  if (stage < 0 || stage > 2) return fail(EIAT_ERR_INVALID_ARG, "unknown backward stage %d", stage);
+  return bwd_impl(1 << stage, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H,
+                  n, d, dv, dtype, scale, mask, window, stream);
 }
 
 const char* attn_status_string(int status) {

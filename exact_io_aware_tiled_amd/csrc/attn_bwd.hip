@@ -107,7 +107,10 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const T* __restrict
           b0 = __uint_as_float(b[w] << 16);
           b1 = __uint_as_float(b[w] & 0xFFFF0000u);
         } else {
-          f16x2 ah = __builtin_bit_cast(f16x2, a[w]), bh = __builtin_bit_cast(f16x2, b[w]);
+          // copy the elements out first: a bit-cast applied directly to a vector
+          // element was compiled into a read of element 0
+          const uint32_t aw = a[w], bw = b[w];
+          const f16x2 ah = __builtin_bit_cast(f16x2, aw), bh = __builtin_bit_cast(f16x2, bw);
           a0 = (float)ah[0];
           a1 = (float)ah[1];
           b0 = (float)bh[0];
@@ -524,7 +527,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 template <typename T, int D, int MASK>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int64_t rows = a.bh * a.n;
-  {
+  if (a.stages & 1) {
     constexpr int CPR = D * Elt<T>::kBytes / 16;
     const int64_t blocks = (rows * CPR + 255) / 256;
     hipLaunchKernelGGL((attn_bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
@@ -533,7 +536,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (a.stages & 2) {
     using C = DkvCfg<T, D>;
     const int num_ktiles = (int)((a.n + C::BNK - 1) / C::BNK);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, MASK>), dim3((unsigned)(num_ktiles * a.bh)),
@@ -545,7 +548,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (a.stages & 4) {
     using C = DqCfg<T, D>;
     const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK>), dim3((unsigned)(num_qtiles * a.bh)),
@@ -554,8 +557,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
                        static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dq),
                        (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
                        a.scale);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 template <typename T, int D>

@@ -45,6 +45,7 @@ struct BwdArgs {
   float qk_scale;    // as FwdArgs
   int qmode;
   float scale;       // c itself (multiplies dQ and dK)
+  int stages;        // bit 0: delta, bit 1: dK/dV, bit 2: dQ
   hipStream_t stream;
 };
 

@@ -118,6 +118,23 @@ EIAT_API eiat_status attn_bwd(const void *q, const void *k, const void *v, const
                      size_t workspace_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
                      int64_t dv, int dtype, float scale, int mask, int64_t window, void *stream);
 
+/*
+ * One step of the reverse procedure, for callers that schedule or time the
+ * steps separately: stage 0 computes delta_i = sum_a dO_ia O_ia into
+ * `workspace`; stage 1 computes dK and dV; stage 2 computes dQ.  Stages 1 and 2
+ * read delta from `workspace`, so stage 0 must have run on the same workspace
+ * (in stream order) first.  attn_bwd is stages 0, 1, 2 in that order.  Outputs
+ * a stage does not write are not read and may hold anything.  Arguments,
+ * validation and errors are those of attn_bwd; an unknown stage is
+ * EIAT_ERR_INVALID_ARG.
+ */
+EIAT_API eiat_status attn_bwd_stage(int stage, const void *q, const void *k, const void *v,
+                                    const void *o, const void *dout, const float *lse, void *dq,
+                                    void *dk, void *dvv, void *workspace, size_t workspace_bytes,
+                                    int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                                    int dtype, float scale, int mask, int64_t window,
+                                    void *stream);
+
 /* Static string naming a status code. */
 EIAT_API const char *attn_status_string(int status);
 

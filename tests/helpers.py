@@ -1,10 +1,16 @@
 """Shared test utilities: tolerances, row sampling, and GPU-vs-oracle comparison.
 
 Tolerances (the bar each GPU result must meet against the fp64 oracle):
-  float32 inputs             : max |err| <= 1e-5 on O and LSE
+  float32 inputs             : max |err| <= 1e-5 on O and LSE for unit-variance
+                               scores (c = 1/sqrt(d) on N(0,1) inputs).  fp32
+                               rounding of a score is proportional to its size, so
+                               for larger scores the bound is 1e-5 * c * sqrt(d).
+                               Gradients: max |err| <= 1e-5 * max(1, max |oracle|).
   bf16 / fp16 inputs, fp32 acc: max |err| <= 2e-2 on O, <= 1e-3 on LSE,
                                and dQ, dK, dV within 5e-2 normwise-relative error
-                               (max |err| / max |oracle| over each (b, h) slice).
+                               (max |err| / max(max |oracle|, 1e-3) over each
+                               (b, h) slice; the floor only matters where the exact
+                               gradient is identically zero, e.g. n = 1).
 """
 from __future__ import annotations
 
@@ -41,15 +47,20 @@ def sample_rows(n: int, count: int, seed: int, must=()) -> np.ndarray:
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def fwd_tolerances(dtype: torch.dtype):
+GRAD_FLOOR = 1e-3
+
+
+def fwd_tolerances(dtype: torch.dtype, score_scale: float = 1.0):
+    """score_scale: c * sqrt(d) * (input std)^2, the std of the scores (1 for the workloads)."""
     if dtype == torch.float32:
-        return TOL_F32, TOL_F32
+        t = TOL_F32 * max(1.0, abs(score_scale))
+        return t, t
     return TOL_O_16, TOL_LSE_16
 
 
-def check_fwd(o_gpu, lse_gpu, y_ref, lse_ref, dtype, what=""):
+def check_fwd(o_gpu, lse_gpu, y_ref, lse_ref, dtype, what="", score_scale: float = 1.0):
     """o_gpu/lse_gpu: numpy float64 of the GPU outputs at the compared rows."""
-    tol_o, tol_l = fwd_tolerances(dtype)
+    tol_o, tol_l = fwd_tolerances(dtype, score_scale)
     err_o = float(np.max(np.abs(o_gpu - y_ref))) if o_gpu.size else 0.0
     err_l = float(np.max(np.abs(lse_gpu - lse_ref))) if lse_gpu.size else 0.0
     assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), f"{what}: non-finite"
@@ -66,7 +77,7 @@ def check_grad(g_gpu, g_ref, dtype, what=""):
     worst = 0.0
     for s in range(g_gpu.shape[0]):
         err = float(np.max(np.abs(g_gpu[s] - g_ref[s])))
-        ref = max(float(np.max(np.abs(g_ref[s]))), 1e-30)
+        ref = max(float(np.max(np.abs(g_ref[s]))), GRAD_FLOOR)
         if dtype == torch.float32:
             bound = TOL_GRAD_F32 * max(1.0, ref)
             assert err <= bound, f"{what}[{s}]: max abs err {err:.3g} > {bound:.3g}"

@@ -16,7 +16,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = A.header_functions()
-    assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+    assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
                           "attn_status_string", "attn_last_error", "attn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -82,6 +82,15 @@ def test_fwd_empty_is_ok_without_gpu(lib):
 ])
 def test_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def test_bwd_stage_rejects_unknown_stage(lib):
+    args = [F, F * 2**20, F * 2**21, F * 2**22, F * 2**23, F * 2**24, F * 2**25, F * 2**26,
+            F * 2**27, F * 2**28, 256, 1, 1, 64, 64, 64, 2, 0.125, 1, 0, None]
+    assert lib.attn_bwd_stage(3, *args) == 1
+    assert lib.attn_bwd_stage(-1, *args) == 1
+    assert b"stage" in lib.attn_last_error()
+    assert lib.attn_bwd_stage(1, *args[:12], -1, *args[13:]) == 1  # n < 0
 
 
 def test_bwd_small_workspace(lib):

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_tiled_amd import attn_bwd, attn_fwd
+from exact_io_aware_tiled_amd import attn_bwd, attn_bwd_workspace_bytes, attn_fwd
 from exact_io_aware_tiled_amd.inputs import WORKLOADS, Workload, make_inputs
 from helpers import announce, check_grad, to64
 
@@ -107,3 +107,18 @@ def test_bwd_train_config_sampled_heads():
     a = (q * dq).sum(dim=(2, 3))
     b = (k * dk).sum(dim=(2, 3))
     assert float((a - b).abs().max()) <= 0.05 * float(a.abs().max()) + 1.0
+
+
+def test_bwd_stages_equal_full_call():
+    """attn_bwd_stage 0, 1, 2 in order gives bitwise the outputs of attn_bwd."""
+    w = Workload("stages", 1, 2, 300, 64, 64, "bf16", "causal", seed=47)
+    inp, (o, lse), grads = run_fwd_bwd(w)
+    q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
+    ws = torch.empty(attn_bwd_workspace_bytes(1, 2, 300), dtype=torch.uint8, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for stage in (0, 1, 2):
+        attn_bwd(q, k, v, o, lse, do, scale=w.c, mask=w.mask, dq=dq, dk=dk, dv=dv, workspace=ws,
+                 stage=stage)
+    torch.cuda.synchronize()
+    for a, b in zip(grads, (dq, dk, dv)):
+        assert torch.equal(a, b)

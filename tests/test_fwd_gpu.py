@@ -27,10 +27,14 @@ def run_fwd(w: Workload, inp=None):
     return inp, o, lse
 
 
+def score_std(w: Workload) -> float:
+    return w.c * w.d ** 0.5 * w.qk_mult ** 2
+
+
 def compare_all_rows(w: Workload, inp, o, lse):
     y, _, _, lref = oracle.fwd(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), w.c, w.mask,
                                w.window)
-    return check_fwd(to64(o), to64(lse), y, lref, DT[w.dtype], w.name)
+    return check_fwd(to64(o), to64(lse), y, lref, DT[w.dtype], w.name, score_std(w))
 
 
 def compare_rows(w: Workload, inp, o, lse, rows, heads=None):
@@ -45,7 +49,7 @@ def compare_rows(w: Workload, inp, o, lse, rows, heads=None):
     rows_t = torch.as_tensor(rows)
     og = to64(o[idx][:, rows_t])
     lg = to64(lse[idx][:, rows_t])
-    errs = check_fwd(og, lg, y, lref, DT[w.dtype], w.name)
+    errs = check_fwd(og, lg, y, lref, DT[w.dtype], w.name, score_std(w))
     return errs, m
 
 
