@@ -29,6 +29,9 @@ CFLAGS = [
     "-fvisibility=hidden",
     # packed fp32 VALU forms are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the kernels rescale and read them with VALU
+    # every tile, which AGPR accumulators would turn into copy traffic
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

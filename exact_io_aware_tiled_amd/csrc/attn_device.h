@@ -104,6 +104,34 @@ struct PChunks {
   }
 };
 
+// Sum of the 16 probabilities of one accumulator block.  fp16: from the packed
+// operand chunks (v_dot2 with (1, 1)), so the normaliser adds exactly the
+// rounded values the value product uses; fp16 rounding (2^-11 relative) keeps
+// LSE well inside its bound even for rows with very few keys.  bf16 rounding
+// (2^-8) does not, so bf16 and float32 add the unrounded fp32 values (as a
+// tree, to keep the dependency chain short).
+template <typename T>
+__device__ inline float chunk_sum(const PChunks<T>& pc, const f32x16& p, float acc) {
+  if constexpr (__is_same(T, _Float16)) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t pw = pc.c[s][w];
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw), one, acc, false);
+      }
+    return acc;
+  } else {
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = p[e] + p[e + 8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] += t[e + 4];
+    return acc + ((t[0] + t[1]) + (t[2] + t[3]));
+  }
+}
+
 // Load the "transposed" operand matching PChunks from an LDS row that stores 32
 // consecutive keys of one output row (row-major over keys, element type T):
 // chunk index ci covers the same keys as PChunks<T>::c[ci] for half-wave h.
@@ -121,7 +149,29 @@ __device__ inline u32x4 keyrow_chunk(const char* row32, int ci, int h) {
   }
 }
 
-__device__ inline float wave_swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// The value held by lane L ^ 32.  v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second; with both operands equal
+// to x, lane L < 32 finds x[L + 32] in the second result and lane L >= 32 finds
+// x[L - 32] in the first.
+__device__ inline float wave_other_half(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+// max / sum over the two half-waves (symmetric, so either result order works)
+__device__ inline float halves_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// True in every lane when `pred` holds in at least one lane of the wave.
+__device__ inline bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

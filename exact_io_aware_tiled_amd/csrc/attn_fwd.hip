@@ -13,18 +13,30 @@
 // (batch, head); each wave owns 32 rows and keeps them in registers as the B
 // operand of S^T = K Q^T, so the accumulator gives every lane all the scores of
 // ONE query row (16 keys per 32-key block per half-wave): the row max and row
-// sum are in-lane, plus one swap of the two half-waves.  Key/value tiles of
-// BN = 64 keys stream through LDS, double-buffered: K row-major, V transposed
-// (V^T, keys contiguous) so that both feed the MFMA without per-element LDS
-// reads.  P = 2^(s*c*log2(e) - m) is rounded to the input type in registers and
-// used directly as the B operand of O^T += V^T P^T (no LDS round trip).  Only O
+// sum are in-lane, plus one exchange of the two half-waves (v_permlane32_swap).
+// Key/value tiles of BN = 64 keys stream through LDS, double-buffered, loaded
+// one tile ahead into registers.  K is read row-major as the A operand of S^T.
+// For 16-bit types V is stored row-major too and read with ds_read_b64_tr_b16,
+// which delivers the V^T operand of O^T += V^T P^T directly; float32 stores a
+// transposed copy instead.  P = 2^(s*c*log2(e) - m) is rounded to the input type
+// in registers and used directly as the B operand (no LDS round trip).  Only O
 // and LSE = m + ln l go to HBM; no score block ever leaves the registers.
+//
+// Deviation from the pages' update, exact in real arithmetic: the running
+// shift m is only raised when a block's maximum exceeds it by more than 2^8 (in
+// base-2 units) for some row of the wave; otherwise the old shift is kept and no
+// rescale is done.  Terms stay below 2^8 (no overflow in fp32 or in the 16-bit
+// operand), and O = z / l and LSE = m + ln l do not depend on which shift was
+// used, only on its consistency, as the merge identity shows.
+//
 // Blocks with no allowed key are not visited (causal / window tile ranges) and
 // the per-element mask is applied only in blocks that straddle a boundary.
 #include "attn_device.h"
 #include "attn_internal.h"
 
 namespace eiat {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, int D>
 struct FwdCfg {
@@ -34,21 +46,47 @@ struct FwdCfg {
   static constexpr int BN = 64;               // keys per tile
   static constexpr int DP = D < 32 ? 32 : D;  // value rows padded to whole 32-row blocks
   static constexpr int S = Elt<T>::kBytes;
+  static constexpr bool kTr = (S == 2);       // 16-bit: V row-major + transpose reads
   static constexpr int KROW = D * S + 16;     // K tile row stride in LDS (bytes), padded
-  static constexpr int VROW = BN * S + 16;    // V^T tile row stride in LDS (bytes), padded
+  // V tile: row-major [BN][DP] (16-bit) or transposed [DP][BN] (float32)
+  static constexpr int VROW = kTr ? DP * S + 16 : BN * S + 16;
   static constexpr int KBYTES = BN * KROW;
-  static constexpr int VBYTES = DP * VROW;
+  static constexpr int VBYTES = (kTr ? BN : DP) * VROW;
   static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int NCH = D * S / 32;      // d-chunks per 32x32 product (both halves)
   static constexpr int NOB = DP / 32;         // 32-row blocks of O^T
   static constexpr int NSB = BN / 32;         // 32-key blocks of S^T
   static constexpr int CPR = D * S / 16;      // 16-byte chunks per K / V row
   static constexpr int KCHUNKS = BN * CPR;
-  static constexpr int VTASKS = (BN / 4) * CPR;  // 4 keys x 16 bytes each
   static constexpr int KPT = (KCHUNKS + kThreads - 1) / kThreads;
+  // V: 16-bit stages 16-byte chunks like K; float32 stages 4-key x 16-byte tasks
+  static constexpr int VTASKS = kTr ? BN * CPR : (BN / 4) * CPR;
+  static constexpr int VREGS = kTr ? 1 : 4;
   static constexpr int VPT = (VTASKS + kThreads - 1) / kThreads;
   static constexpr int EPC = 16 / S;          // elements per 16-byte chunk
+  static constexpr float kTau = 8.0f;         // lazy-rescale threshold, base-2 units
 };
+
+// V^T operand chunk ci (0, 1) of the 32-key block at key offset kbase and value
+// rows [32 ob, 32 ob + 32), read from a row-major V tile with two transpose reads.
+// Lane L = 16 G + j addresses row kbase + 16 ci + 8 c + 4 (G / 2) + j / 4 and
+// columns 32 ob + 16 (G % 2) + 4 (j % 4) .. + 3 for read c; the transpose read
+// then hands lane L the 4 consecutive keys 16 ci + 8 c + 4 h + (0..3) of value
+// column 32 ob + L % 32 -- the key slots of PChunks.
+__device__ inline u32x4 vt_chunk_tr(const char* vtile, int vrow_bytes, int kbase, int ob, int ci,
+                                    int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const int col = 32 * ob + 16 * (G & 1) + 4 * (j & 3);
+  const int row = kbase + 16 * ci + 4 * (G >> 1) + (j >> 2);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const char* p0 = vtile + row * vrow_bytes + col * 2;
+  const char* p1 = p0 + 8 * vrow_bytes;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
+  return r;
+}
 
 template <typename T, int D, int MASK>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
@@ -93,48 +131,58 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
   // This wave's query rows as MFMA B-operand chunks: lane L holds row qw0 + L%32,
   // d-bytes [32c + 16h, 32c + 16h + 16).  The sign of c is folded into Q
   // (qmode 1), and c = 0 is taken as Q = 0 with a unit exponent scale (qmode 2).
+  // Rows past n read row n - 1 (never stored).
   u32x4 qf[C::NCH];
+  {
+    const int qr = min(qrow, n - 1);
 #pragma unroll
-  for (int c = 0; c < C::NCH; ++c) {
-    qf[c] = qrow < n ? ldg16(Qh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
-    if (qmode == 1) qf[c] ^= Elt<T>::kSign;
-    if (qmode == 2) qf[c] = zero4();
+    for (int c = 0; c < C::NCH; ++c) {
+      qf[c] = ldg16(Qh + (int64_t)qr * D * C::S + 32 * c + 16 * h);
+      if (qmode == 1) qf[c] ^= Elt<T>::kSign;
+      if (qmode == 2) qf[c] = zero4();
+    }
   }
 
-  // Value rows beyond D (only for D < 32) stay zero in both buffers.
+  // Value columns/rows beyond D (only for D < 32) stay zero in both buffers.
   if constexpr (C::DP > D) {
-    for (int idx = tid; idx < 2 * (C::DP - D) * (C::VROW / 16); idx += C::kThreads) {
-      int b = idx / ((C::DP - D) * (C::VROW / 16));
-      int rem = idx % ((C::DP - D) * (C::VROW / 16));
-      int row = D + rem / (C::VROW / 16);
-      int col = rem % (C::VROW / 16);
-      *reinterpret_cast<u32x4*>(smem + b * C::BUF + C::KBYTES + row * C::VROW + col * 16) = zero4();
+    constexpr int zrows = C::kTr ? BN : C::DP - D;
+    constexpr int zper = C::kTr ? (C::DP - D) * C::S / 16 : C::VROW / 16;
+    for (int idx = tid; idx < 2 * zrows * zper; idx += C::kThreads) {
+      const int b = idx / (zrows * zper), rem = idx % (zrows * zper);
+      const int row = rem / zper, col = rem % zper;
+      char* vb = smem + b * C::BUF + C::KBYTES;
+      if constexpr (C::kTr)
+        *reinterpret_cast<u32x4*>(vb + row * C::VROW + D * C::S + col * 16) = zero4();
+      else
+        *reinterpret_cast<u32x4*>(vb + (D + row) * C::VROW + col * 16) = zero4();
     }
   }
 
   u32x4 kreg[C::KPT];
-  u32x4 vreg[C::VPT][4];
+  u32x4 vreg[C::VPT][C::VREGS];
 
+  // Rows past n are read from row n - 1: they are masked (K) or multiplied by a
+  // zero probability (V), so the loads need no branch.
   auto load_tile = [&](int t) {
     const int j0 = t * BN;
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
       const int c = tid + r * C::kThreads;
-      if (c < C::KCHUNKS) {
+      if (C::KCHUNKS % C::kThreads == 0 || c < C::KCHUNKS) {
         const int key = c / C::CPR, col = c % C::CPR;
-        const int j = j0 + key;
-        kreg[r] = j < n ? ldg16(Kh + (int64_t)j * D * C::S + col * 16) : zero4();
+        const int j = min(j0 + key, n - 1);
+        kreg[r] = ldg16(Kh + (int64_t)j * D * C::S + col * 16);
       }
     }
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
       const int task = tid + r * C::kThreads;
-      if (task < C::VTASKS) {
+      if (C::VTASKS % C::kThreads == 0 || task < C::VTASKS) {
         const int kq = task / C::CPR, col = task % C::CPR;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 4 * kq + i;
-          vreg[r][i] = j < n ? ldg16(Vh + (int64_t)j * D * C::S + col * 16) : zero4();
+        for (int i = 0; i < C::VREGS; ++i) {
+          const int j = min(j0 + C::VREGS * kq + i, n - 1);
+          vreg[r][i] = ldg16(Vh + (int64_t)j * D * C::S + col * 16);
         }
       }
     }
@@ -146,7 +194,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
       const int c = tid + r * C::kThreads;
-      if (c < C::KCHUNKS) {
+      if (C::KCHUNKS % C::kThreads == 0 || c < C::KCHUNKS) {
         const int key = c / C::CPR, col = c % C::CPR;
         *reinterpret_cast<u32x4*>(kb + key * C::KROW + col * 16) = kreg[r];
       }
@@ -154,15 +202,18 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
       const int task = tid + r * C::kThreads;
-      if (task < C::VTASKS) {
+      if (C::VTASKS % C::kThreads == 0 || task < C::VTASKS) {
         const int kq = task / C::CPR, col = task % C::CPR;
-        store_transposed4<T>(vb + (col * C::EPC) * C::VROW + 4 * kq * C::S, C::VROW, vreg[r]);
+        if constexpr (C::kTr)
+          *reinterpret_cast<u32x4*>(vb + kq * C::VROW + col * 16) = vreg[r][0];
+        else
+          store_transposed4<T>(vb + (col * C::EPC) * C::VROW + 4 * kq * C::S, C::VROW, vreg[r]);
       }
     }
   };
 
-  // Running summary of this lane's query row (both half-waves keep identical m;
-  // each keeps a partial l over its own keys; the partials are added at the end).
+  // Running summary of this lane's query row.  Both half-waves keep the same
+  // shift m; each keeps a partial l over its own keys (added at the end).
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x16 o[C::NOB];
@@ -223,38 +274,39 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
       for (int sb = 0; sb < C::NSB; ++sb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
-      mx = fmaxf(mx, wave_swap_halves(mx));
+      mx = halves_max(mx);
       const float m_blk = (mx == -INFINITY) ? -INFINITY : mx * qk_scale;
-      const float m_new = fmaxf(m_run, m_blk);
+      // Raise the shift (and rescale) only if some row's max grew by more than tau.
+      if (wave_any(m_blk > m_run + C::kTau)) {
+        const float m_new = fmaxf(m_run, m_blk);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+        m_run = m_new;
+      }
       // A row with no allowed key so far keeps the empty summary: shift by 0.
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
 
-      float rsum = 0.0f;
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
-          s[sb][e] = p;
-          rsum += p;
-        }
-      l_run = l_run * alpha + rsum;
-#pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
-
-      // O^T += V^T P^T
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
         PChunks<T> pc;
         pc.set(s[sb]);
+        l_run = chunk_sum<T>(pc, s[sb], l_run);
+        // O^T += V^T P^T over this 32-key block
 #pragma unroll
         for (int ob = 0; ob < C::NOB; ++ob) {
-          const char* vrow = vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S;
 #pragma unroll
-          for (int ci = 0; ci < PChunks<T>::kCount; ++ci)
-            o[ob] = Elt<T>::mma(keyrow_chunk<T>(vrow, ci, h), pc.c[ci], o[ob]);
+          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+            u32x4 va;
+            if constexpr (C::kTr)
+              va = vt_chunk_tr(vb, C::VROW, 32 * sb, ob, ci, lane);
+            else
+              va = keyrow_chunk<T>(vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S, ci, h);
+            o[ob] = Elt<T>::mma(va, pc.c[ci], o[ob]);
+          }
         }
       }
     }
@@ -264,7 +316,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
   }
 
   // Epilogue: O = z / l in the input type, LSE = m + ln l (natural log).
-  const float l_tot = l_run + wave_swap_halves(l_run);
+  const float l_tot = halves_sum(l_run);
   if (qrow < n) {
     const float inv = 1.0f / l_tot;
     char* orow = reinterpret_cast<char*>(O + (head + qrow) * D);
@@ -326,7 +378,5 @@ hipError_t launch_fwd(const FwdArgs& a) {
     default: return launch_fwd_dt<__bf16>(a);
   }
 }
-
-int64_t fwd_max_blocks_per_bh(int64_t n) { return (n + FwdCfg<float, 64>::BM - 1) / FwdCfg<float, 64>::BM; }
 
 }  // namespace eiat
