@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="page_d64")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
+                    help="override a workload field, e.g. --set n=16384 --set mask=none")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -135,6 +137,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = WORKLOADS[args.workload]
+    for kv in args.set:
+        key, val = kv.split("=", 1)
+        cur = getattr(w, key)
+        w = w.replace(**{key: type(cur)(val) if cur is not None else float(val)})
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = attn.load_library()

@@ -170,6 +170,19 @@ __device__ inline float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Maximum of the NSB * 16 accumulator values of a lane, as four independent
+// running maxima (each folds into v_max3 without operand canonicalisation)
+// combined at the end, so the reduction is not one long dependency chain.
+template <int NSB>
+__device__ inline float tile_max(const f32x16 (&s)[NSB]) {
+  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m[e & 3] = fmaxf(m[e & 3], s[sb][e]);
+  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+}
+
 // True in every lane when `pred` holds in at least one lane of the wave.
 __device__ inline bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

@@ -31,6 +31,8 @@
 //
 // Blocks with no allowed key are not visited (causal / window tile ranges) and
 // the per-element mask is applied only in blocks that straddle a boundary.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -40,7 +42,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, int D>
 struct FwdCfg {
-  static constexpr int kWaves = 4;
+  // 16-bit d = 128 shares each K/V tile among 8 waves (256 query rows); the
+  // others use 4 waves (128 rows), which balances the causal grid better.
+  static constexpr int kWaves = (D >= 128 && Elt<T>::kBytes == 2) ? 8 : 4;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 32 * kWaves;      // query rows per workgroup
   static constexpr int BN = 64;               // keys per tile
@@ -52,7 +56,6 @@ struct FwdCfg {
   static constexpr int VROW = kTr ? DP * S + 16 : BN * S + 16;
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = (kTr ? BN : DP) * VROW;
-  static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int NCH = D * S / 32;      // d-chunks per 32x32 product (both halves)
   static constexpr int NOB = DP / 32;         // 32-row blocks of O^T
   static constexpr int NSB = BN / 32;         // 32-key blocks of S^T
@@ -65,6 +68,10 @@ struct FwdCfg {
   static constexpr int VPT = (VTASKS + kThreads - 1) / kThreads;
   static constexpr int EPC = 16 / S;          // elements per 16-byte chunk
   static constexpr float kTau = 8.0f;         // lazy-rescale threshold, base-2 units
+  // Waves per SIMD the register allocation must allow (4-wave workgroups)
+  // (bf16 at d <= 64 fits three; fp16 needs a few more registers for its sums)
+  static constexpr int kMinWaves =
+      S == 4 ? (D >= 128 ? 1 : 2) : ((D >= 128 || !__is_same(T, __bf16)) ? 2 : 3);
 };
 
 // V^T operand chunk ci (0, 1) of the 32-key block at key offset kbase and value
@@ -89,7 +96,10 @@ __device__ inline u32x4 vt_chunk_tr(const char* vtile, int vrow_bytes, int kbase
 }
 
 template <typename T, int D, int MASK>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
+__global__ void
+    __attribute__((amdgpu_flat_work_group_size(1, FwdCfg<T, D>::kThreads),
+                   amdgpu_waves_per_eu(FwdCfg<T, D>::kMinWaves, 8)))
+    attn_fwd_kernel(const T* __restrict__ Q,
                                                        const T* __restrict__ K,
                                                        const T* __restrict__ V,
                                                        T* __restrict__ O, float* __restrict__ LSE,
@@ -97,7 +107,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
                                                        int window, float qk_scale, int qmode) {
   using C = FwdCfg<T, D>;
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+  // LDS: two K buffers, then two V buffers.  K runs one tile ahead of V.
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::KBYTES + 2 * C::VBYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,6 +138,14 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
   if (MASK == 2) kbeg = max(0, q0 - window + 1);
   const int t_lo = kbeg / BN;
   const int t_hi = (kend + BN - 1) / BN;
+  // Tiles in [t_in_lo, t_in_hi) need no per-element mask for any row of the
+  // workgroup (every key allowed and below n); the others are boundary tiles.
+  int t_in_lo = t_lo, t_in_hi = t_hi;
+  if (MASK == 2) t_in_lo = max(t_lo, (q0 + C::BM - 1 - window + 1 + BN - 1) / BN);
+  if (MASK != 0) t_in_hi = min(t_hi, (q0 + 1) / BN);
+  t_in_hi = min(t_in_hi, n / BN);
+  t_in_lo = min(t_in_lo, t_hi);
+  if (t_in_hi < t_in_lo) t_in_hi = t_in_lo;
 
   // This wave's query rows as MFMA B-operand chunks: lane L holds row qw0 + L%32,
   // d-bytes [32c + 16h, 32c + 16h + 16).  The sign of c is folded into Q
@@ -143,14 +162,17 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
     }
   }
 
-  // Value columns/rows beyond D (only for D < 32) stay zero in both buffers.
+  auto kbuf = [&](int t) __attribute__((always_inline)) -> char* { return smem + (t & 1) * C::KBYTES; };
+  auto vbuf = [&](int t) __attribute__((always_inline)) -> char* { return smem + 2 * C::KBYTES + (t & 1) * C::VBYTES; };
+
+  // Value columns/rows beyond D (only for D < 32) stay zero in both V buffers.
   if constexpr (C::DP > D) {
     constexpr int zrows = C::kTr ? BN : C::DP - D;
     constexpr int zper = C::kTr ? (C::DP - D) * C::S / 16 : C::VROW / 16;
     for (int idx = tid; idx < 2 * zrows * zper; idx += C::kThreads) {
       const int b = idx / (zrows * zper), rem = idx % (zrows * zper);
       const int row = rem / zper, col = rem % zper;
-      char* vb = smem + b * C::BUF + C::KBYTES;
+      char* vb = vbuf(b);
       if constexpr (C::kTr)
         *reinterpret_cast<u32x4*>(vb + row * C::VROW + D * C::S + col * 16) = zero4();
       else
@@ -163,7 +185,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
 
   // Rows past n are read from row n - 1: they are masked (K) or multiplied by a
   // zero probability (V), so the loads need no branch.
-  auto load_tile = [&](int t) {
+  auto load_k = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
@@ -174,6 +196,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
         kreg[r] = ldg16(Kh + (int64_t)j * D * C::S + col * 16);
       }
     }
+  };
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * BN;
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
       const int task = tid + r * C::kThreads;
@@ -187,10 +212,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
       }
     }
   };
-
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * C::BUF;
-    char* vb = kb + C::KBYTES;
+  auto store_k = [&](int t) __attribute__((always_inline)) {
+    char* kb = kbuf(t);
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
       const int c = tid + r * C::kThreads;
@@ -199,6 +222,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
         *reinterpret_cast<u32x4*>(kb + key * C::KROW + col * 16) = kreg[r];
       }
     }
+  };
+  auto store_v = [&](int t) __attribute__((always_inline)) {
+    char* vb = vbuf(t);
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
       const int task = tid + r * C::kThreads;
@@ -208,6 +234,21 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
           *reinterpret_cast<u32x4*>(vb + kq * C::VROW + col * 16) = vreg[r][0];
         else
           store_transposed4<T>(vb + (col * C::EPC) * C::VROW + 4 * kq * C::S, C::VROW, vreg[r]);
+      }
+    }
+  };
+
+  // S^T block of tile t = K_t Q_w^T (fp32 accumulate)
+  auto qk = [&](int t, f32x16 (&s)[C::NSB]) {
+    const char* kb = kbuf(t);
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[sb][e] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c) {
+        u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * sb + l32) * C::KROW + 32 * c + 16 * h);
+        s[sb] = Elt<T>::mma(a, qf[c], s[sb]);
       }
     }
   };
@@ -222,98 +263,111 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[ob][e] = 0.0f;
 
-  load_tile(t_lo);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
-
+  // Merging the scores s of tile t into the running summary is split in two so
+  // that the next tile's score MFMAs can be issued between the halves:
+  // prep_tile masks (boundary tiles only), takes the block max and, if needed,
+  // raises the shift and rescales; exp_pv_tile forms P = 2^(s c log2 e - m),
+  // adds its sum to l and accumulates O^T += V^T P^T.  A tile with no allowed
+  // key for some row leaves that row unchanged (its P is 0), as the
+  // Algorithm's empty-block skip does.
+  auto prep_tile = [&](int t, f32x16 (&s)[C::NSB], auto masked) -> float {
     const int j0 = t * BN;
-    // The Algorithm's empty-block skip at wave granularity.
-    bool empty = false;
-    if (MASK != 0) empty = j0 > qw0 + 31;
-    if (MASK == 2) empty = empty || (j0 + BN - 1 < qw0 - window + 1);
-
-    if (!empty) {
-      const char* kb = smem + buf * C::BUF;
-      const char* vb = kb + C::KBYTES;
-
-      // S^T block = K_tile Q_w^T (fp32 accumulate)
-      f32x16 s[C::NSB];
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[sb][e] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < C::NCH; ++c) {
-          u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * sb + l32) * C::KROW + 32 * c + 16 * h);
-          s[sb] = Elt<T>::mma(a, qf[c], s[sb]);
-        }
-      }
-
-      // Per-element mask only where the tile straddles a boundary.
-      bool straddle = j0 + BN > n;
-      if (MASK != 0) straddle = straddle || (j0 + BN - 1 > qw0);
-      if (MASK == 2) straddle = straddle || (j0 < qw0 + 31 - window + 1);
-      if (straddle) {
-#pragma unroll
-        for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (!key_allowed<MASK>(qrow, j, n, window)) s[sb][e] = -INFINITY;
-          }
-      }
-
-      // Block maximum of this row, in units of log2 (c * log2(e) folded in).
-      float mx = -INFINITY;
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
-      mx = halves_max(mx);
-      const float m_blk = (mx == -INFINITY) ? -INFINITY : mx * qk_scale;
-      // Raise the shift (and rescale) only if some row's max grew by more than tau.
-      if (wave_any(m_blk > m_run + C::kTau)) {
-        const float m_new = fmaxf(m_run, m_blk);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (!key_allowed<MASK>(qrow, j, n, window)) s[sb][e] = -INFINITY;
+        }
+    }
+    // Block maximum of this row, in units of log2 (c * log2(e) folded in),
+    // as a shallow tree so the reduction is not one long dependency chain.
+    float mx = halves_max(tile_max<C::NSB>(s));
+    const float m_blk = (mx == -INFINITY) ? -INFINITY : mx * qk_scale;
+    // Raise the shift (and rescale) only if some row's max grew by more than tau.
+    if (wave_any(m_blk > m_run + C::kTau)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-        for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
-        m_run = m_new;
-      }
-      // A row with no allowed key so far keeps the empty summary: shift by 0.
-      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-
+      for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+      m_run = m_new;
+    }
+    // A row with no allowed key so far keeps the empty summary: shift by 0.
+    return (m_run == -INFINITY) ? 0.0f : m_run;
+  };
+  auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use) {
+    const char* vb = vbuf(t);
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
+    for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
-        PChunks<T> pc;
-        pc.set(s[sb]);
-        l_run = chunk_sum<T>(pc, s[sb], l_run);
-        // O^T += V^T P^T over this 32-key block
+      for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
+      PChunks<T> pc;
+      pc.set(s[sb]);
+      l_run = chunk_sum<T>(pc, s[sb], l_run);
 #pragma unroll
-        for (int ob = 0; ob < C::NOB; ++ob) {
+      for (int ob = 0; ob < C::NOB; ++ob) {
 #pragma unroll
-          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
-            u32x4 va;
-            if constexpr (C::kTr)
-              va = vt_chunk_tr(vb, C::VROW, 32 * sb, ob, ci, lane);
-            else
-              va = keyrow_chunk<T>(vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S, ci, h);
-            o[ob] = Elt<T>::mma(va, pc.c[ci], o[ob]);
-          }
+        for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+          u32x4 va;
+          if constexpr (C::kTr)
+            va = vt_chunk_tr(vb, C::VROW, 32 * sb, ob, ci, lane);
+          else
+            va = keyrow_chunk<T>(vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S, ci, h);
+          o[ob] = Elt<T>::mma(va, pc.c[ci], o[ob]);
         }
       }
     }
+  };
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+  // Prologue: K_lo, V_lo and K_lo+1 in LDS, S_lo in registers.
+  f32x16 sbuf[2][C::NSB];
+  load_k(t_lo);
+  load_v(t_lo);
+  store_k(t_lo);
+  store_v(t_lo);
+  if (t_lo + 1 < t_hi) {
+    load_k(t_lo + 1);
+    store_k(t_lo + 1);
   }
+  __syncthreads();
+  qk(t_lo, sbuf[0]);
+  __syncthreads();  // K_lo is overwritten by K_lo+2 in the first iteration
+
+  // Iteration t: S_{t+1} = K_{t+1} Q^T is formed while S_t is exponentiated, then
+  // V_{t+1} and K_{t+2} (loaded from HBM at the top) are stored for the next one.
+  // The next tile's scores are formed in the second score buffer and moved to
+  // the first at the end of the iteration (indices are compile-time constants so
+  // both stay in registers).
+  auto iterate = [&](int t, auto parity, auto masked) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    const bool has1 = t + 1 < t_hi, has2 = t + 2 < t_hi;
+    if (has1) load_v(t + 1);
+    if (has2) load_k(t + 2);
+    const float m_use = prep_tile(t, sbuf[P], masked);
+    // Raised priority while this wave has MFMAs to issue, so another wave's
+    // softmax VALU work fills the gaps rather than delaying them.
+    __builtin_amdgcn_s_setprio(1);
+    qk(t + 1, sbuf[1 - P]);  // t + 1 == t_hi reads a stale buffer; the result is unused
+    exp_pv_tile(t, sbuf[P], m_use);
+    __builtin_amdgcn_s_setprio(0);
+    if (has1) store_v(t + 1);
+    if (has2) store_k(t + 2);
+    __syncthreads();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  auto run = [&](int t, int end, auto masked) __attribute__((always_inline)) -> int {
+    for (; t < end; ++t) {
+      iterate(t, P0{}, masked);
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) sbuf[0][sb] = sbuf[1][sb];
+    }
+    return t;
+  };
+  int t = run(t_lo, t_in_lo, std::true_type{});
+  t = run(t, t_in_hi, std::false_type{});
+  run(t, t_hi, std::true_type{});
 
   // Epilogue: O = z / l in the input type, LSE = m + ln l (natural log).
   const float l_tot = halves_sum(l_run);
