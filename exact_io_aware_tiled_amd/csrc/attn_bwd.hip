@@ -19,8 +19,9 @@
 //   3. dQ: a workgroup keeps 128 query rows (Q, dO, LSE, delta) in registers
 //      and streams key/value tiles through LDS, as the forward does, with
 //      dQ^T += K^T dS^T.
-// Transposed LDS copies (dO^T, Q^T, K^T) are written while staging, from the
-// same registers that hold the natural copies.
+// The transposed operands (dO^T, Q^T, K^T) are read from the natural LDS tiles
+// with ds_read_b64_tr_b16 for 16-bit types; float32 writes transposed copies
+// while staging, from the same registers that hold the natural copies.
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -69,6 +70,17 @@ struct Stager {
     }
   }
 };
+
+// Zero columns [D, DP) of every row of a natural tile (only when D < 32): the
+// transpose reads of output rows [D, DP) then see zeros.
+template <int D, int DP, int S, int ROWS, int NROW, int THREADS>
+__device__ inline void zero_pad_cols(char* nat, int tid) {
+  if constexpr (DP > D) {
+    constexpr int per_row = (DP - D) * S / 16;
+    for (int idx = tid; idx < ROWS * per_row; idx += THREADS)
+      *reinterpret_cast<u32x4*>(nat + (idx / per_row) * NROW + D * S + (idx % per_row) * 16) = zero4();
+  }
+}
 
 // Zero rows [D, DP) of a transposed tile (only when D < 32).
 template <int D, int DP, int TROW, int THREADS>
@@ -140,13 +152,17 @@ struct DkvCfg {
   static constexpr int BMQ = D >= 128 ? 32 : 64;     // query rows per streamed tile
   static constexpr int DP = D < 32 ? 32 : D;
   static constexpr int S = Elt<T>::kBytes;
-  static constexpr int NROW = D * S + 16;            // Q / dO natural rows
-  static constexpr int TROW = BMQ * S + 16;          // Q^T / dO^T rows
+  // 16-bit: Q^T and dO^T operands come from the natural tiles through transpose
+  // reads; float32 keeps transposed copies.
+  static constexpr bool kTr = (S == 2);
+  static constexpr int NROW = (kTr ? DP : D) * S + 16;  // Q / dO natural rows
+  static constexpr int TROW = BMQ * S + 16;             // Q^T / dO^T rows (float32)
+  static constexpr int TBYTES = kTr ? 0 : DP * TROW;
   static constexpr int QN = 0;
   static constexpr int QT = QN + BMQ * NROW;
-  static constexpr int ON = QT + DP * TROW;
+  static constexpr int ON = QT + TBYTES;
   static constexpr int OT = ON + BMQ * NROW;
-  static constexpr int LS = OT + DP * TROW;          // LSE * log2(e), BMQ floats
+  static constexpr int LS = OT + TBYTES;             // LSE * log2(e), BMQ floats
   static constexpr int DL = LS + BMQ * 4;            // delta, BMQ floats
   static constexpr int BUF = DL + BMQ * 4;
   static constexpr int NCH = D * S / 32;
@@ -163,7 +179,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
   using C = DkvCfg<T, D>;
   constexpr int BMQ = C::BMQ;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
-  using St = Stager<T, D, BMQ, C::kThreads, C::NROW, C::TROW, true, true>;
+  using St = Stager<T, D, BMQ, C::kThreads, C::NROW, C::TROW, true, !C::kTr>;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bid = blockIdx.x;
@@ -207,10 +223,16 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
       dv[ob][e] = 0.0f;
     }
 
-  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::QT, tid);
-  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::OT, tid);
-  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::BUF + C::QT, tid);
-  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::BUF + C::OT, tid);
+  for (int b = 0; b < 2; ++b) {
+    char* base = smem + b * C::BUF;
+    if constexpr (C::kTr) {
+      zero_pad_cols<D, C::DP, C::S, BMQ, C::NROW, C::kThreads>(base + C::QN, tid);
+      zero_pad_cols<D, C::DP, C::S, BMQ, C::NROW, C::kThreads>(base + C::ON, tid);
+    } else {
+      zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(base + C::QT, tid);
+      zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(base + C::OT, tid);
+    }
+  }
 
   St sq, so;
   float4 lreg, dreg;  // LSE * log2(e) and delta for 4 rows (threads < BMQ / 4)
@@ -309,12 +331,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
         dsc.set(dp);
 #pragma unroll
         for (int ob = 0; ob < C::NOB; ++ob) {
-          const char* orow = b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S;
-          const char* qrow = b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S;
 #pragma unroll
           for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
-            dv[ob] = Elt<T>::mma(keyrow_chunk<T>(orow, ci, h), pc.c[ci], dv[ob]);
-            dk[ob] = Elt<T>::mma(keyrow_chunk<T>(qrow, ci, h), dsc.c[ci], dk[ob]);
+            u32x4 oa, qa2;
+            if constexpr (C::kTr) {
+              oa = tr_chunk(b + C::ON, C::NROW, 32 * qb, ob, ci, lane);
+              qa2 = tr_chunk(b + C::QN, C::NROW, 32 * qb, ob, ci, lane);
+            } else {
+              oa = keyrow_chunk<T>(b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
+              qa2 = keyrow_chunk<T>(b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
+            }
+            dv[ob] = Elt<T>::mma(oa, pc.c[ci], dv[ob]);
+            dk[ob] = Elt<T>::mma(qa2, dsc.c[ci], dk[ob]);
           }
         }
       }
@@ -363,11 +391,14 @@ struct DqCfg {
   static constexpr int S = Elt<T>::kBytes;
   static constexpr int BN = (S == 4 && D >= 128) ? 32 : 64;  // keys per streamed tile
   static constexpr int DP = D < 32 ? 32 : D;
-  static constexpr int NROW = D * S + 16;   // K, V natural rows
-  static constexpr int TROW = BN * S + 16;  // K^T rows
+  // 16-bit: the K^T operand comes from the natural K tile through transpose
+  // reads; float32 keeps a transposed copy.
+  static constexpr bool kTr = (S == 2);
+  static constexpr int NROW = (kTr ? DP : D) * S + 16;  // K, V natural rows
+  static constexpr int TROW = BN * S + 16;              // K^T rows (float32)
   static constexpr int KN = 0;
   static constexpr int KT = KN + BN * NROW;
-  static constexpr int VN = KT + DP * TROW;
+  static constexpr int VN = KT + (kTr ? 0 : DP * TROW);
   static constexpr int BUF = VN + BN * NROW;
   static constexpr int NCH = D * S / 32;
   static constexpr int NOB = DP / 32;
@@ -383,7 +414,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
   using C = DqCfg<T, D>;
   constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
-  using StK = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, true>;
+  using StK = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, !C::kTr>;
   using StV = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, false>;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -423,8 +454,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[ob][e] = 0.0f;
 
-  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::KT, tid);
-  zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + C::BUF + C::KT, tid);
+  for (int b = 0; b < 2; ++b) {
+    if constexpr (C::kTr)
+      zero_pad_cols<D, C::DP, C::S, BN, C::NROW, C::kThreads>(smem + b * C::BUF + C::KN, tid);
+    else
+      zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + b * C::BUF + C::KT, tid);
+  }
 
   StK sk;
   StV sv;
@@ -488,10 +523,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
         dsc.set(dp);
 #pragma unroll
         for (int ob = 0; ob < C::NOB; ++ob) {
-          const char* krow = b + C::KT + (32 * ob + l32) * C::TROW + 32 * sb * C::S;
 #pragma unroll
-          for (int ci = 0; ci < PChunks<T>::kCount; ++ci)
-            dq[ob] = Elt<T>::mma(keyrow_chunk<T>(krow, ci, h), dsc.c[ci], dq[ob]);
+          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+            u32x4 ka2;
+            if constexpr (C::kTr)
+              ka2 = tr_chunk(b + C::KN, C::NROW, 32 * sb, ob, ci, lane);
+            else
+              ka2 = keyrow_chunk<T>(b + C::KT + (32 * ob + l32) * C::TROW + 32 * sb * C::S, ci, h);
+            dq[ob] = Elt<T>::mma(ka2, dsc.c[ci], dq[ob]);
+          }
         }
       }
     }

@@ -149,6 +149,32 @@ __device__ inline u32x4 keyrow_chunk(const char* row32, int ci, int h) {
   }
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed operand from a row-major 16-bit tile X[r][col] (row stride
+// vrow_bytes): the MFMA A-operand chunk ci (0, 1) of X^T for output rows
+// [32 ob, 32 ob + 32) and the 32 contraction rows starting at kbase, with the
+// contraction slots of PChunks.  Two ds_read_b64_tr_b16 per chunk.
+// Lane L = 16 G + j addresses row kbase + 16 ci + 8 c + 4 (G / 2) + j / 4 and
+// columns 32 ob + 16 (G % 2) + 4 (j % 4) .. + 3 for read c; within each group of
+// 16 lanes the read hands lane j element (j % 4) of the rows addressed by lanes
+// j / 4 + {0, 4, 8, 12} (layout checked on the GPU), i.e. lane L receives rows
+// 16 ci + 8 c + 4 h + (0..3) of column 32 ob + L % 32.
+__device__ inline u32x4 tr_chunk(const char* vtile, int vrow_bytes, int kbase, int ob, int ci,
+                                    int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const int col = 32 * ob + 16 * (G & 1) + 4 * (j & 3);
+  const int row = kbase + 16 * ci + 4 * (G >> 1) + (j >> 2);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const char* p0 = vtile + row * vrow_bytes + col * 2;
+  const char* p1 = p0 + 8 * vrow_bytes;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
+  return r;
+}
+
 // The value held by lane L ^ 32.  v_permlane32_swap exchanges the upper half of
 // its first operand with the lower half of its second; with both operands equal
 // to x, lane L < 32 finds x[L + 32] in the second result and lane L >= 32 finds

@@ -38,8 +38,6 @@
 
 namespace eiat {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
 template <typename T, int D>
 struct FwdCfg {
   // 16-bit d = 128 shares each K/V tile among 8 waves (256 query rows); the
@@ -73,27 +71,6 @@ struct FwdCfg {
   static constexpr int kMinWaves =
       S == 4 ? (D >= 128 ? 1 : 2) : ((D >= 128 || !__is_same(T, __bf16)) ? 2 : 3);
 };
-
-// V^T operand chunk ci (0, 1) of the 32-key block at key offset kbase and value
-// rows [32 ob, 32 ob + 32), read from a row-major V tile with two transpose reads.
-// Lane L = 16 G + j addresses row kbase + 16 ci + 8 c + 4 (G / 2) + j / 4 and
-// columns 32 ob + 16 (G % 2) + 4 (j % 4) .. + 3 for read c; the transpose read
-// then hands lane L the 4 consecutive keys 16 ci + 8 c + 4 h + (0..3) of value
-// column 32 ob + L % 32 -- the key slots of PChunks.
-__device__ inline u32x4 vt_chunk_tr(const char* vtile, int vrow_bytes, int kbase, int ob, int ci,
-                                    int lane) {
-  const int G = lane >> 4, j = lane & 15;
-  const int col = 32 * ob + 16 * (G & 1) + 4 * (j & 3);
-  const int row = kbase + 16 * ci + 4 * (G >> 1) + (j >> 2);
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const char* p0 = vtile + row * vrow_bytes + col * 2;
-  const char* p1 = p0 + 8 * vrow_bytes;
-  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-  u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-  u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
-  return r;
-}
 
 template <typename T, int D, int MASK>
 __global__ void
@@ -312,7 +289,7 @@ __global__ void
         for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
           u32x4 va;
           if constexpr (C::kTr)
-            va = vt_chunk_tr(vb, C::VROW, 32 * sb, ob, ci, lane);
+            va = tr_chunk(vb, C::VROW, 32 * sb, ob, ci, lane);
           else
             va = keyrow_chunk<T>(vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S, ci, h);
           o[ob] = Elt<T>::mma(va, pc.c[ci], o[ob]);
