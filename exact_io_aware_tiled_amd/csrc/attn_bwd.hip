@@ -168,17 +168,25 @@ struct DkvCfg {
   static constexpr int NCH = D * S / 32;
   static constexpr int NOB = DP / 32;
   static constexpr int NQB = BMQ / 32;
+  // 16-bit tiles without zero-padded columns go HBM -> LDS directly
+  static constexpr bool kDirect = kTr && D >= 32;
+  // d = 128 (16-bit): the workgroup's V rows stay in LDS and are read per query
+  // tile instead of being held in registers, so two waves fit per SIMD.
+  static constexpr bool kVLds = kDirect && D >= 128;
+  static constexpr int VRES = 2 * BUF;                 // resident V rows
+  static constexpr int SMEM = 2 * BUF + (kVLds ? BNK * NROW : 0);
 };
 
 template <typename T, int D, int MASK>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(Elt<T>::kBytes == 2 ? 2 : 1, 8))) attn_bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     T* __restrict__ dK, T* __restrict__ dV, int n, int bh_count, int num_ktiles, int window,
     float qk_scale, int qmode, float scale) {
   using C = DkvCfg<T, D>;
   constexpr int BMQ = C::BMQ;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   using St = Stager<T, D, BMQ, C::kThreads, C::NROW, C::TROW, true, !C::kTr>;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -199,14 +207,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
   const float* LSEh = LSE + head;
   const float* Dh = delta + head;
 
-  // This wave's 32 keys of K and V as B-operand chunks (lane: key kw0 + L%32).
-  u32x4 kf[C::NCH], vf[C::NCH];
+  // This wave's 32 keys of K and V as B-operand chunks (lane: key kw0 + L%32);
+  // with kVLds the V rows go to LDS instead and are read back per query tile.
+  u32x4 kf[C::NCH], vf[C::kVLds ? 1 : C::NCH];
 #pragma unroll
   for (int c = 0; c < C::NCH; ++c) {
     kf[c] = key < n ? ldg16(Kh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
-    vf[c] = key < n ? ldg16(Vh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
+    if constexpr (!C::kVLds)
+      vf[c] = key < n ? ldg16(Vh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
     if (qmode == 1) kf[c] ^= Elt<T>::kSign;
   }
+  if constexpr (C::kVLds)
+    tile_to_lds<32, D * C::S / 16, 1>(smem + C::VRES + 32 * wave * C::NROW, Vh, kw0, n, 0, lane);
 
   // Query rows that may see any key of this workgroup.
   int qbeg = 0, qend = n;
@@ -239,8 +251,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
 
   auto load_tile = [&](int t) {
     const int r0 = t * BMQ;
-    sq.load(Qh, r0, n, tid);
-    so.load(dOh, r0, n, tid);
+    if constexpr (C::kDirect) {
+      char* b = smem + ((t - t_lo) & 1) * C::BUF;
+      tile_to_lds<BMQ, D * C::S / 16, C::kWaves>(b + C::QN, Qh, r0, n, wave, lane);
+      tile_to_lds<BMQ, D * C::S / 16, C::kWaves>(b + C::ON, dOh, r0, n, wave, lane);
+    } else {
+      sq.load(Qh, r0, n, tid);
+      so.load(dOh, r0, n, tid);
+    }
     if (tid < BMQ / 4) {
       float* lr = reinterpret_cast<float*>(&lreg);
       float* dr = reinterpret_cast<float*>(&dreg);
@@ -255,8 +273,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
   };
   auto store_tile = [&](int buf) {
     char* b = smem + buf * C::BUF;
-    sq.store(b + C::QN, b + C::QT, tid);
-    so.store(b + C::ON, b + C::OT, tid);
+    if constexpr (C::kDirect) {
+      wait_tile_loads();
+    } else {
+      sq.store(b + C::QN, b + C::QT, tid);
+      so.store(b + C::ON, b + C::OT, tid);
+    }
     if (tid < BMQ / 4) {
       *reinterpret_cast<float4*>(b + C::LS + 16 * tid) = lreg;
       *reinterpret_cast<float4*>(b + C::DL + 16 * tid) = dreg;
@@ -300,7 +322,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(
           u32x4 qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
           u32x4 oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
           if (qmode != 2) s = Elt<T>::mma(qa, kf[c], s);
-          dp = Elt<T>::mma(oa, vf[c], dp);
+          u32x4 vb4;
+          if constexpr (C::kVLds)
+            vb4 = *reinterpret_cast<const u32x4*>(smem + C::VRES + (32 * wave + l32) * C::NROW +
+                                                  32 * c + 16 * h);
+          else
+            vb4 = vf[c];
+          dp = Elt<T>::mma(oa, vb4, dp);
         }
         if (straddle) {
 #pragma unroll
@@ -403,6 +431,7 @@ struct DqCfg {
   static constexpr int NCH = D * S / 32;
   static constexpr int NOB = DP / 32;
   static constexpr int NSB = BN / 32;
+  static constexpr bool kDirect = kTr && D >= 32;
 };
 
 template <typename T, int D, int MASK>
@@ -464,13 +493,23 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
   StK sk;
   StV sv;
   auto load_tile = [&](int t) {
-    sk.load(Kh, t * BN, n, tid);
-    sv.load(Vh, t * BN, n, tid);
+    if constexpr (C::kDirect) {
+      char* b = smem + ((t - t_lo) & 1) * C::BUF;
+      tile_to_lds<BN, D * C::S / 16, C::kWaves>(b + C::KN, Kh, t * BN, n, wave, lane);
+      tile_to_lds<BN, D * C::S / 16, C::kWaves>(b + C::VN, Vh, t * BN, n, wave, lane);
+    } else {
+      sk.load(Kh, t * BN, n, tid);
+      sv.load(Vh, t * BN, n, tid);
+    }
   };
   auto store_tile = [&](int buf) {
-    char* b = smem + buf * C::BUF;
-    sk.store(b + C::KN, b + C::KT, tid);
-    sv.store(b + C::VN, nullptr, tid);
+    if constexpr (C::kDirect) {
+      wait_tile_loads();
+    } else {
+      char* b = smem + buf * C::BUF;
+      sk.store(b + C::KN, b + C::KT, tid);
+      sv.store(b + C::VN, nullptr, tid);
+    }
   };
 
   load_tile(t_lo);

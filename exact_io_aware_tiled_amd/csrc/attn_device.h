@@ -151,6 +151,40 @@ __device__ inline u32x4 keyrow_chunk(const char* row32, int ci, int h) {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+// Copy rows [r0, r0 + R) of a [n][C * 16 bytes] global slice into an LDS tile
+// whose rows are C 16-byte chunks plus one padding chunk, with the gfx950
+// direct-to-LDS load (global_load_lds_dwordx4): wave instruction i writes the
+// 1 KiB [1024 i, 1024 i + 1024) of the tile, lane l its 16-byte slot 64 i + l
+// (placement checked on the GPU).  Slots map onto whole rows; a padding slot
+// fetches a duplicate of its row's first chunk, and lanes past the last slot
+// of a partly used final instruction are switched off.  Rows past n read row
+// n - 1.  The data is in LDS once the issuing wave's vector-memory count has
+// drained (wait_tile_loads) and a barrier has passed.
+template <int R, int C, int WAVES>
+__device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, int n, int wave,
+                                   int lane) {
+  constexpr int kSlots = R * (C + 1);
+  constexpr int kInstr = (kSlots + 63) / 64;
+  typedef const void __attribute__((address_space(1)))* gptr_t;
+  typedef void __attribute__((address_space(3)))* lptr_t;
+#pragma unroll
+  for (int i0 = 0; i0 < kInstr; i0 += WAVES) {
+    const int i = i0 + wave;
+    if (kInstr % WAVES == 0 || i < kInstr) {
+      const int slot = 64 * i + lane;
+      if (kSlots % 64 == 0 || slot < kSlots) {
+        const int row = slot / (C + 1), c = slot % (C + 1);
+        const int gr = min(r0 + row, n - 1);
+        const char* src = gbase + (int64_t)gr * (C * 16) + (c < C ? c : 0) * 16;
+        __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lds_tile + 1024 * i), 16, 0, 0);
+      }
+    }
+  }
+}
+
+// Wait until this wave's direct-to-LDS loads have landed.
+__device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Transposed operand from a row-major 16-bit tile X[r][col] (row stride
 // vrow_bytes): the MFMA A-operand chunk ci (0, 1) of X^T for output rows
 // [32 ob, 32 ob + 32) and the 32 contraction rows starting at kbase, with the

@@ -14,8 +14,9 @@
 // operand of S^T = K Q^T, so the accumulator gives every lane all the scores of
 // ONE query row (16 keys per 32-key block per half-wave): the row max and row
 // sum are in-lane, plus one exchange of the two half-waves (v_permlane32_swap).
-// Key/value tiles of BN = 64 keys stream through LDS, double-buffered, loaded
-// one tile ahead into registers.  K is read row-major as the A operand of S^T.
+// Key/value tiles of BN = 64 keys stream through LDS, double-buffered: 16-bit
+// tiles with d >= 32 are copied HBM -> LDS directly (global_load_lds_dwordx4,
+// no staging registers); the others are staged one tile ahead in registers.  K is read row-major as the A operand of S^T.
 // For 16-bit types V is stored row-major too and read with ds_read_b64_tr_b16,
 // which delivers the V^T operand of O^T += V^T P^T directly; float32 stores a
 // transposed copy instead.  P = 2^(s*c*log2(e) - m) is rounded to the input type
@@ -65,6 +66,8 @@ struct FwdCfg {
   static constexpr int VREGS = kTr ? 1 : 4;
   static constexpr int VPT = (VTASKS + kThreads - 1) / kThreads;
   static constexpr int EPC = 16 / S;          // elements per 16-byte chunk
+  // 16-bit tiles without zero-padded columns go HBM -> LDS directly
+  static constexpr bool kDirect = kTr && D >= 32;
   static constexpr float kTau = 8.0f;         // lazy-rescale threshold, base-2 units
   // Waves per SIMD the register allocation must allow (4-wave workgroups)
   // (bf16 at d <= 64 fits three; fp16 needs a few more registers for its sums)
@@ -157,13 +160,17 @@ __global__ void
     }
   }
 
-  u32x4 kreg[C::KPT];
-  u32x4 vreg[C::VPT][C::VREGS];
+  u32x4 kreg[C::kDirect ? 1 : C::KPT];
+  u32x4 vreg[C::kDirect ? 1 : C::VPT][C::VREGS];
 
   // Rows past n are read from row n - 1: they are masked (K) or multiplied by a
   // zero probability (V), so the loads need no branch.
   auto load_k = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
+    if constexpr (C::kDirect) {
+      tile_to_lds<BN, C::CPR, C::kWaves>(kbuf(t), Kh, j0, n, wave, lane);
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
       const int c = tid + r * C::kThreads;
@@ -176,6 +183,10 @@ __global__ void
   };
   auto load_v = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
+    if constexpr (C::kDirect) {
+      tile_to_lds<BN, C::CPR, C::kWaves>(vbuf(t), Vh, j0, n, wave, lane);
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
       const int task = tid + r * C::kThreads;
@@ -190,6 +201,10 @@ __global__ void
     }
   };
   auto store_k = [&](int t) __attribute__((always_inline)) {
+    if constexpr (C::kDirect) {
+      wait_tile_loads();
+      return;
+    }
     char* kb = kbuf(t);
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
@@ -201,6 +216,10 @@ __global__ void
     }
   };
   auto store_v = [&](int t) __attribute__((always_inline)) {
+    if constexpr (C::kDirect) {
+      wait_tile_loads();
+      return;
+    }
     char* vb = vbuf(t);
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
