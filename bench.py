@@ -66,8 +66,9 @@ def sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
-    """Counter-derived HBM bytes per launch, if taken on the current kernel sources."""
+def load_traffic(kernel: str, workload) -> float | None:
+    """Counter-derived HBM bytes per launch, if taken on the current kernel
+    sources and on this exact workload (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
@@ -75,6 +76,8 @@ def load_traffic(kernel: str):
         return None
     entry = data.get("kernels", {}).get(kernel)
     if not entry or data.get("sources_sha") != sources_digest():
+        return None
+    if data.get("workload") != repr(workload):
         return None
     return entry.get("bytes_per_launch")
 
@@ -232,7 +235,7 @@ def main():
         achieved = amount / (kern_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = load_traffic(dom)
+    roof["traffic"] = load_traffic(dom, w)
 
     per_kernel = {}
     for name, ms in kern_ms.items():
