@@ -216,6 +216,7 @@ __global__ void __launch_bounds__(256)
     if constexpr (!C::kVLds)
       vf[c] = key < n ? ldg16(Vh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
     if (qmode == 1) kf[c] ^= Elt<T>::kSign;
+    if (qmode == 2) kf[c] = zero4();  // c = 0: every score is exactly 0
   }
   if constexpr (C::kVLds)
     tile_to_lds<32, D * C::S / 16, 1>(smem + C::VRES + 32 * wave * C::NROW, Vh, kw0, n, 0, lane);
@@ -265,9 +266,11 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + 4 * tid + i;
+        const int rc = min(r, n - 1);
+        const float lv = LSEh[rc] * kLog2e, dv0 = Dh[rc];
         // rows past n contribute nothing: p = 2^(-inf) = 0
-        lr[i] = r < n ? LSEh[r] * kLog2e : INFINITY;
-        dr[i] = r < n ? Dh[r] : 0.0f;
+        lr[i] = r < n ? lv : INFINITY;
+        dr[i] = r < n ? dv0 : 0.0f;
       }
     }
   };
@@ -321,7 +324,7 @@ __global__ void __launch_bounds__(256)
         for (int c = 0; c < C::NCH; ++c) {
           u32x4 qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
           u32x4 oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
-          if (qmode != 2) s = Elt<T>::mma(qa, kf[c], s);
+          s = Elt<T>::mma(qa, kf[c], s);
           u32x4 vb4;
           if constexpr (C::kVLds)
             vb4 = *reinterpret_cast<const u32x4*>(smem + C::VRES + (32 * wave + l32) * C::NROW +
@@ -467,6 +470,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
     qf[c] = qrow < n ? ldg16(Qh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
     of[c] = qrow < n ? ldg16(dOh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
     if (qmode == 1) qf[c] ^= Elt<T>::kSign;
+    if (qmode == 2) qf[c] = zero4();  // c = 0: every score is exactly 0
   }
   const float lse2 = qrow < n ? LSE[head + qrow] * kLog2e : INFINITY;
   const float dlt = qrow < n ? delta[head + qrow] : 0.0f;
@@ -543,7 +547,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
         for (int c = 0; c < C::NCH; ++c) {
           u32x4 ka = *reinterpret_cast<const u32x4*>(b + C::KN + rk * C::NROW + 32 * c + 16 * h);
           u32x4 va = *reinterpret_cast<const u32x4*>(b + C::VN + rk * C::NROW + 32 * c + 16 * h);
-          if (qmode != 2) s = Elt<T>::mma(ka, qf[c], s);
+          s = Elt<T>::mma(ka, qf[c], s);
           dp = Elt<T>::mma(va, of[c], dp);
         }
         if (straddle) {
