@@ -189,7 +189,8 @@ __global__ void __launch_bounds__(256)
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   using St = Stager<T, D, BMQ, C::kThreads, C::NROW, C::TROW, true, !C::kTr>;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
   const int bh = bid % bh_count;
   int kt = bid / bh_count;
@@ -247,6 +248,8 @@ __global__ void __launch_bounds__(256)
     }
   }
 
+  TileLoader<BMQ, D * C::S / 16, C::kWaves> tl;
+  if constexpr (C::kDirect) tl.init(wave, lane);
   St sq, so;
   float4 lreg, dreg;  // LSE * log2(e) and delta for 4 rows (threads < BMQ / 4)
 
@@ -254,8 +257,8 @@ __global__ void __launch_bounds__(256)
     const int r0 = t * BMQ;
     if constexpr (C::kDirect) {
       char* b = smem + ((t - t_lo) & 1) * C::BUF;
-      tile_to_lds<BMQ, D * C::S / 16, C::kWaves>(b + C::QN, Qh, r0, n, wave, lane);
-      tile_to_lds<BMQ, D * C::S / 16, C::kWaves>(b + C::ON, dOh, r0, n, wave, lane);
+      tl.load(b + C::QN, Qh, r0, n, wave, lane);
+      tl.load(b + C::ON, dOh, r0, n, wave, lane);
     } else {
       sq.load(Qh, r0, n, tid);
       so.load(dOh, r0, n, tid);
@@ -449,7 +452,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
   using StK = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, !C::kTr>;
   using StV = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, false>;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
   const int bh = bid % bh_count;
   int qt = bid / bh_count;
@@ -494,13 +498,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
       zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + b * C::BUF + C::KT, tid);
   }
 
+  TileLoader<BN, D * C::S / 16, C::kWaves> tl;
+  if constexpr (C::kDirect) tl.init(wave, lane);
   StK sk;
   StV sv;
   auto load_tile = [&](int t) {
     if constexpr (C::kDirect) {
       char* b = smem + ((t - t_lo) & 1) * C::BUF;
-      tile_to_lds<BN, D * C::S / 16, C::kWaves>(b + C::KN, Kh, t * BN, n, wave, lane);
-      tile_to_lds<BN, D * C::S / 16, C::kWaves>(b + C::VN, Vh, t * BN, n, wave, lane);
+      tl.load(b + C::KN, Kh, t * BN, n, wave, lane);
+      tl.load(b + C::VN, Vh, t * BN, n, wave, lane);
     } else {
       sk.load(Kh, t * BN, n, tid);
       sv.load(Vh, t * BN, n, tid);

@@ -160,13 +160,33 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // of a partly used final instruction are switched off.  Rows past n read row
 // n - 1.  The data is in LDS once the issuing wave's vector-memory count has
 // drained (wait_tile_loads) and a barrier has passed.
+//
+// The load is issued from inline assembly rather than the compiler builtin:
+// the compiler cannot tell which LDS bytes such a load writes, so after the
+// builtin it drains the vector-memory count before the next transposing LDS
+// read (ds_read_b64_tr_b16) of ANY tile, which turns every prefetch into a
+// synchronous load.  Issued this way the load is invisible to the compiler's
+// wait insertion; every tile written here is read only after an explicit
+// wait_tile_loads() and a barrier.  M0 (the LDS base of the load) is set in
+// the same statement; no compiler-generated code in these kernels uses M0.
+__device__ inline void lds_dma16(const char* src, char* lds_dst) {
+  typedef char __attribute__((address_space(3)))* lds_char_t;
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t)lds_dst);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 template <int R, int C, int WAVES>
 __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, int n, int wave,
                                    int lane) {
   constexpr int kSlots = R * (C + 1);
   constexpr int kInstr = (kSlots + 63) / 64;
-  typedef const void __attribute__((address_space(1)))* gptr_t;
-  typedef void __attribute__((address_space(3)))* lptr_t;
 #pragma unroll
   for (int i0 = 0; i0 < kInstr; i0 += WAVES) {
     const int i = i0 + wave;
@@ -176,11 +196,60 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
         const int row = slot / (C + 1), c = slot % (C + 1);
         const int gr = min(r0 + row, n - 1);
         const char* src = gbase + (int64_t)gr * (C * 16) + (c < C ? c : 0) * 16;
-        __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lds_tile + 1024 * i), 16, 0, 0);
+        lds_dma16(src, lds_tile + 1024 * i);
       }
     }
   }
 }
+
+// The same copy for tiles whose rows all lie below n, with the cheaper
+// addressing form of the direct load: a wave-uniform 64-bit base in SGPRs
+// (the tile's first row) plus a per-lane 32-bit offset that depends only on
+// the lane's slot and is computed once (init).  Per tile only scalar
+// arithmetic changes; load() falls back to tile_to_lds for a tile that runs
+// past row n - 1.  `wave` must be wave-uniform (e.g. from readfirstlane).
+template <int R, int C, int WAVES>
+struct TileLoader {
+  static constexpr int kSlots = R * (C + 1);
+  static constexpr int kInstr = (kSlots + 63) / 64;
+  static constexpr int kPer = (kInstr + WAVES - 1) / WAVES;
+  uint32_t off[kPer];
+
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int slot = 64 * (k * WAVES + wave) + lane;
+      const int row = slot / (C + 1), c = slot % (C + 1);
+      off[k] = (uint32_t)(row * (C * 16) + (c < C ? c : 0) * 16);
+    }
+  }
+
+  __device__ inline void load(char* lds_tile, const char* gbase, int r0, int n, int wave,
+                              int lane) const {
+    if (r0 + R > n) {
+      tile_to_lds<R, C, WAVES>(lds_tile, gbase, r0, n, wave, lane);
+      return;
+    }
+    const char* g = gbase + (int64_t)r0 * (C * 16);
+    typedef char __attribute__((address_space(3)))* lds_char_t;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = k * WAVES + wave;
+      if (kInstr % WAVES == 0 || i < kInstr) {
+        if (kSlots % 64 == 0 || 64 * i + lane < kSlots) {
+          const uint32_t m0v = (uint32_t)(uintptr_t)(lds_char_t)(lds_tile + 1024 * i);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+          asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                       :
+                       : "v"(off[k]), "s"(g), "s"(m0v)
+                       : "memory", "m0");
+#pragma clang diagnostic pop
+        }
+      }
+    }
+  }
+};
 
 // Wait until this wave's direct-to-LDS loads have landed.
 __device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -69,6 +69,9 @@ struct FwdCfg {
   // 16-bit tiles without zero-padded columns go HBM -> LDS directly
   static constexpr bool kDirect = kTr && D >= 32;
   static constexpr float kTau = 8.0f;         // lazy-rescale threshold, base-2 units
+  // Two score buffers (next tile's scores issued before this tile's
+  // exponentials) where the score MFMAs are long enough to hide the exp work.
+  static constexpr bool kDoubleS = D >= 128;
   // Waves per SIMD the register allocation must allow (4-wave workgroups)
   // (bf16 at d <= 64 fits three; fp16 needs a few more registers for its sums)
   static constexpr int kMinWaves =
@@ -92,7 +95,7 @@ __global__ void
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -160,6 +163,8 @@ __global__ void
     }
   }
 
+  TileLoader<BN, C::CPR, C::kWaves> tl;
+  if constexpr (C::kDirect) tl.init(wave, lane);
   u32x4 kreg[C::kDirect ? 1 : C::KPT];
   u32x4 vreg[C::kDirect ? 1 : C::VPT][C::VREGS];
 
@@ -168,7 +173,7 @@ __global__ void
   auto load_k = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
     if constexpr (C::kDirect) {
-      tile_to_lds<BN, C::CPR, C::kWaves>(kbuf(t), Kh, j0, n, wave, lane);
+      tl.load(kbuf(t), Kh, j0, n, wave, lane);
       return;
     }
 #pragma unroll
@@ -184,7 +189,7 @@ __global__ void
   auto load_v = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
     if constexpr (C::kDirect) {
-      tile_to_lds<BN, C::CPR, C::kWaves>(vbuf(t), Vh, j0, n, wave, lane);
+      tl.load(vbuf(t), Vh, j0, n, wave, lane);
       return;
     }
 #pragma unroll
@@ -318,7 +323,7 @@ __global__ void
   };
 
   // Prologue: K_lo, V_lo and K_lo+1 in LDS, S_lo in registers.
-  f32x16 sbuf[2][C::NSB];
+  f32x16 sc[C::kDoubleS ? 2 : 1][C::NSB];
   load_k(t_lo);
   load_v(t_lo);
   store_k(t_lo);
@@ -328,37 +333,43 @@ __global__ void
     store_k(t_lo + 1);
   }
   __syncthreads();
-  qk(t_lo, sbuf[0]);
+  qk(t_lo, sc[0]);
   __syncthreads();  // K_lo is overwritten by K_lo+2 in the first iteration
 
-  // Iteration t: S_{t+1} = K_{t+1} Q^T is formed while S_t is exponentiated, then
-  // V_{t+1} and K_{t+2} (loaded from HBM at the top) are stored for the next one.
-  // The next tile's scores are formed in the second score buffer and moved to
-  // the first at the end of the iteration (indices are compile-time constants so
-  // both stay in registers).
-  auto iterate = [&](int t, auto parity, auto masked) __attribute__((always_inline)) {
-    constexpr int P = decltype(parity)::value;
+  // Iteration t: the scores of tile t are exponentiated and multiplied into O
+  // while S_{t+1} = K_{t+1} Q^T is formed; V_{t+1} and K_{t+2}, loaded from HBM
+  // at the top, are stored for the next iteration.  With one score buffer
+  // S_{t+1} overwrites S_t after its exponentials (the scheduler interleaves
+  // those MFMAs with the second half of the tile); with two (d = 128, twice
+  // the MFMA work per tile) S_{t+1} is issued first into the second buffer and
+  // moved to the first at the end of the iteration.
+  auto iterate = [&](int t, auto masked) __attribute__((always_inline)) {
     const bool has1 = t + 1 < t_hi, has2 = t + 2 < t_hi;
     if (has1) load_v(t + 1);
     if (has2) load_k(t + 2);
-    const float m_use = prep_tile(t, sbuf[P], masked);
+    const float m_use = prep_tile(t, sc[0], masked);
     // Raised priority while this wave has MFMAs to issue, so another wave's
     // softmax VALU work fills the gaps rather than delaying them.
     __builtin_amdgcn_s_setprio(1);
-    qk(t + 1, sbuf[1 - P]);  // t + 1 == t_hi reads a stale buffer; the result is unused
-    exp_pv_tile(t, sbuf[P], m_use);
+    // t + 1 == t_hi reads a stale buffer; the result is unused
+    if constexpr (C::kDoubleS) {
+      qk(t + 1, sc[C::kDoubleS ? 1 : 0]);
+      exp_pv_tile(t, sc[0], m_use);
+    } else {
+      exp_pv_tile(t, sc[0], m_use);
+      qk(t + 1, sc[0]);
+    }
     __builtin_amdgcn_s_setprio(0);
     if (has1) store_v(t + 1);
     if (has2) store_k(t + 2);
     __syncthreads();
-  };
-  using P0 = std::integral_constant<int, 0>;
-  auto run = [&](int t, int end, auto masked) __attribute__((always_inline)) -> int {
-    for (; t < end; ++t) {
-      iterate(t, P0{}, masked);
+    if constexpr (C::kDoubleS) {
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) sbuf[0][sb] = sbuf[1][sb];
+      for (int sb = 0; sb < C::NSB; ++sb) sc[0][sb] = sc[C::kDoubleS ? 1 : 0][sb];
     }
+  };
+  auto run = [&](int t, int end, auto masked) __attribute__((always_inline)) -> int {
+    for (; t < end; ++t) iterate(t, masked);
     return t;
   };
   int t = run(t_lo, t_in_lo, std::true_type{});
