@@ -17,6 +17,14 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libeiat_attn.so")
 SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip"]
+# Machine-scheduler strategy per source, chosen by timing each kernel file's
+# kernels under the strategies LLVM offers for AMDGPU: the forward's
+# exp/MFMA interleave does best under max-ilp, the backward kernels (many
+# LDS reads feeding each MFMA group) under max-memory-clause.
+PER_SOURCE_FLAGS = {
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+}
 ARCH = os.environ.get("EIAT_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,7 +46,8 @@ CFLAGS = [
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *PER_SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
