@@ -70,6 +70,9 @@ def _load():
         lib.oracle_fwd_tiled.argtypes = [i64, i64, i64, i64, ip, ip, ip, dbl, ctypes.c_int, i64,
                                          i64, ctypes.c_int, ip, ip, ip]
         lib.oracle_fwd_tiled.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = [i64, i64, i64, i64, i64, i64, i64, ip, ip, ip, dbl,
+                                      ctypes.c_int, i64, ip, ip]
+        lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -118,6 +121,22 @@ def fwd(q, k, v, scale: float, mask="none", window: int = 0, rows=None):
                           int(window), rp, nrows, _ptr(y), _ptr(m), _ptr(l), _ptr(lse)), "fwd")
     shp = lead + (nrows,)
     return y.reshape(shp + (dv,)), m.reshape(shp), l.reshape(shp), lse.reshape(shp)
+
+
+def decode(q, k, v, scale: float, mask="none", window: int = 0):
+    """Decode-shaped forward: q [B, H, nq, d] are the last nq positions of a
+    sequence whose keys/values k, v [B, Hkv, nk, d|dv] are all cached; H must be
+    a multiple of Hkv.  Returns (Y [B, H, nq, dv], LSE [B, H, nq])."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, nq, d = q.shape
+    _, Hkv, nk, _ = k.shape
+    dv = v.shape[-1]
+    y = np.empty((B, H, nq, dv))
+    lse = np.empty((B, H, nq))
+    _check(lib.oracle_decode(B, H, Hkv, nq, nk, d, dv, _ptr(q), _ptr(k), _ptr(v), float(scale),
+                             _mask_code(mask), int(window), _ptr(y), _ptr(lse)), "decode")
+    return y, lse
 
 
 def bwd(q, k, v, g, scale: float, mask="none", window: int = 0):

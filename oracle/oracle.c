@@ -15,6 +15,9 @@
  *        section "Streaming softmax" (the running max / running sum update).
  *  [NS]  harperz9.github.io, Night School "Fused attention", section
  *        "Forget one step" (the broken-rescale control).
+ *  [WT]  webturing.com.tr Principia, "Bellek Duvarinin Fizigi: Standart
+ *        Attention'dan FlashAttention'a", section on the KV cache, long context
+ *        and approximate attention (decode-shaped rows against a key cache).
  *
  * Conventions (readings of the pages, also listed in the design notes):
  *  - Rows and keys are 0-based here; the pages index from 1.
@@ -67,14 +70,14 @@ static double score(const double *qi, const double *kj, int64_t d, double c)
  * One row of the dense definition ([AM] Theorem "Tiled attention ... are exact",
  * the displayed dense masked attention row, with the max shift of step 2.1):
  *   m_i = max_{j in A_i} s_ij,  l_i = sum_{j in A_i} e^{s_ij - m_i},
- *   Y_i = sum_{j in A_i} (e^{s_ij - m_i} / l_i) V_j.
- * srow is caller scratch of length n.
+ *   Y_i = sum_{j in A_i} (e^{s_ij - m_i} / l_i) V_j,
+ * for the query vector qi sitting at row position i (A_i is the mask's set for
+ * position i over keys 0..n-1).  srow is caller scratch of length n.
  */
-static void dense_row(const double *Q, const double *K, const double *V, int64_t n, int64_t d,
-                      int64_t dv, double c, int mask, int64_t window, int64_t i, double *srow,
-                      double *y, double *m_out, double *l_out)
+static void dense_row_at(const double *qi, const double *K, const double *V, int64_t n,
+                         int64_t d, int64_t dv, double c, int mask, int64_t window, int64_t i,
+                         double *srow, double *y, double *m_out, double *l_out)
 {
-    const double *qi = Q + i * d;
     double m = -INFINITY;
     for (int64_t j = 0; j < n; j++) {
         if (!in_allowed(mask, window, i, j)) continue;
@@ -95,6 +98,14 @@ static void dense_row(const double *Q, const double *K, const double *V, int64_t
     }
     *m_out = m;
     *l_out = l;
+}
+
+/* Row i of the dense definition with its own query vector Q_i. */
+static void dense_row(const double *Q, const double *K, const double *V, int64_t n, int64_t d,
+                      int64_t dv, double c, int mask, int64_t window, int64_t i, double *srow,
+                      double *y, double *m_out, double *l_out)
+{
+    dense_row_at(Q + i * d, K, V, n, d, dv, c, mask, window, i, srow, y, m_out, l_out);
 }
 
 /*
@@ -132,6 +143,56 @@ int oracle_fwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
                 if (M) M[h * nrows + r] = m;
                 if (L) L[h * nrows + r] = l;
                 if (LSE) LSE[h * nrows + r] = m + log(l);
+            }
+        }
+        free(srow);
+    }
+    return failed ? OR_ENOMEM : OR_OK;
+}
+
+/*
+ * Decode-shaped forward: nq new query rows per head against a cache of nk keys
+ * (1 <= nq <= nk), the rows being the LAST nq positions of the sequence, so row
+ * i sits at position p_i = nk - nq + i and its allowed set is the mask's set
+ * for position p_i over keys 0..nk-1 (the KV-cache setting of [WT], section on
+ * the KV cache and long context, where every new token attends to the cached
+ * keys and values of all earlier tokens; [AI] on verifying several new
+ * positions in one pass).  H query heads share Hkv key/value heads: query head
+ * h reads key/value head h / (H / Hkv) (H a multiple of Hkv; Hkv = H is one
+ * head each).  Every row is the dense definition above at position p_i.
+ * Layout: Q [B][H][nq][d], K [B][Hkv][nk][d], V [B][Hkv][nk][dv];
+ * outputs Y [B][H][nq][dv] and LSE [B][H][nq] (LSE may be NULL).
+ */
+int oracle_decode(int64_t B, int64_t H, int64_t Hkv, int64_t nq, int64_t nk, int64_t d,
+                  int64_t dv, const double *Q, const double *K, const double *V, double c,
+                  int mask, int64_t window, double *Y, double *LSE)
+{
+    if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || nq < 1 || nk < nq) return OR_EINVAL;
+    if (check_args(B * H, nk, d, dv, mask, window)) return OR_EINVAL;
+    const int64_t G = H / Hkv;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *srow = (double *)malloc(sizeof(double) * (size_t)nk);
+        if (srow == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for collapse(3) schedule(dynamic, 4)
+        for (int64_t b = 0; b < B; b++) {
+            for (int64_t h = 0; h < H; h++) {
+                for (int64_t i = 0; i < nq; i++) {
+                    if (srow == NULL) continue;
+                    const int64_t hk = h / G;
+                    const double *qi = Q + ((b * H + h) * nq + i) * d;
+                    const double *Kh = K + (b * Hkv + hk) * nk * d;
+                    const double *Vh = V + (b * Hkv + hk) * nk * dv;
+                    const int64_t row = (b * H + h) * nq + i;
+                    double m, l;
+                    dense_row_at(qi, Kh, Vh, nk, d, dv, c, mask, window, nk - nq + i, srow,
+                                 Y + row * dv, &m, &l);
+                    if (LSE) LSE[row] = m + log(l);
+                }
             }
         }
         free(srow);
