@@ -63,6 +63,11 @@ def load_library():
     lib.attn_bwd_stage.restype = c_int
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64,
+                                i64, i64, c_int, c_float, c_int, i64, vp]
+    lib.attn_decode.restype = c_int
+    lib.attn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -149,3 +154,38 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "ca
     else:
         _check(lib.attn_bwd_stage(int(stage), *args))
     return dq, dk, dv
+
+
+def attn_decode_workspace_bytes(B: int, H: int, Hkv: int, nq: int, nk: int, dv: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, H, Hkv, nq, nk, dv))
+
+
+def attn_decode(q, k, v, scale: Optional[float] = None, mask: str = "none", window: int = 0,
+                out=None, lse=None, workspace=None, stream=None):
+    """O, LSE for nq new rows against a key/value cache.
+
+    q: [B, H, nq, d] (the last nq positions); k: [B, Hkv, nk, d]; v: [B, Hkv, nk, dv];
+    H a multiple of Hkv (query head h reads key/value head h // (H // Hkv)).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-d")
+    B, H, nq, d = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    dv = v.shape[-1]
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty(B, H, nq, dv, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    ws_bytes = attn_decode_workspace_bytes(B, H, Hkv, nq, nk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H,
+                           Hkv, nq, nk, d, dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask],
+                           int(window), _stream_handle(stream)))
+    return out, lse

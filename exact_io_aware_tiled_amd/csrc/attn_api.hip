@@ -213,6 +213,108 @@ eiat_status attn_bwd_stage(int stage, const void* q, const void* k, const void* 
                   n, d, dv, dtype, scale, mask, window, stream);
 }
 
+size_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t nq, int64_t nk,
+                                   int64_t dv) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || nq <= 0 || nk <= 0 || dv <= 0 || H % Hkv != 0) return 0;
+  const int64_t units = B * Hkv, M = H / Hkv * nq;
+  const int64_t S = eiat::decode_splits(units, nk);
+  return (size_t)units * (size_t)S * (size_t)M * (size_t)(dv + 2) * sizeof(float);
+}
+
+eiat_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                        int64_t Hkv, int64_t nq, int64_t nk, int64_t d, int64_t dv, int dtype,
+                        float scale, int mask, int64_t window, void* stream) {
+  if (B < 0 || nq < 0 || nk < 0) return fail(EIAT_ERR_INVALID_ARG, "B, nq and nk must be >= 0");
+  if (H < 1 || Hkv < 1) return fail(EIAT_ERR_INVALID_ARG, "H and Hkv must be >= 1");
+  if (H % Hkv != 0)
+    return fail(EIAT_ERR_INVALID_ARG, "H (%lld) must be a multiple of Hkv (%lld)", (long long)H,
+                (long long)Hkv);
+  if (nq > nk)
+    return fail(EIAT_ERR_INVALID_ARG, "the nq = %lld new rows are the last of nk = %lld positions",
+                (long long)nq, (long long)nk);
+  if (d < 1 || dv < 1) return fail(EIAT_ERR_INVALID_ARG, "d and dv must be >= 1");
+  if (dtype != EIAT_F32 && dtype != EIAT_F16 && dtype != EIAT_BF16)
+    return fail(EIAT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (mask != EIAT_MASK_NONE && mask != EIAT_MASK_CAUSAL && mask != EIAT_MASK_WINDOW)
+    return fail(EIAT_ERR_INVALID_ARG, "unknown mask kind %d", mask);
+  if (mask == EIAT_MASK_WINDOW && window < 1)
+    return fail(EIAT_ERR_INVALID_ARG, "window must be >= 1 (got %lld)", (long long)window);
+  if (!isfinite(scale)) return fail(EIAT_ERR_INVALID_ARG, "scale must be finite");
+  if (dtype == EIAT_F32) return fail(EIAT_ERR_UNSUPPORTED, "decode kernels take f16 or bf16");
+  if (d != dv || (d != 64 && d != 128))
+    return fail(EIAT_ERR_UNSUPPORTED, "decode kernels take d == dv in {64, 128}");
+  if (H / Hkv * nq > 32)
+    return fail(EIAT_ERR_UNSUPPORTED, "(H / Hkv) * nq = %lld rows per key/value head exceeds 32",
+                (long long)(H / Hkv * nq));
+  if (nk > (int64_t)INT32_MAX - 1024) return fail(EIAT_ERR_UNSUPPORTED, "nk too large");
+  if (B > 0 && H > (int64_t)INT32_MAX / 64 / B) return fail(EIAT_ERR_UNSUPPORTED, "B * H too large");
+  if (B * Hkv > 0 && nk > INT64_MAX / (B * Hkv) / d / 4)
+    return fail(EIAT_ERR_UNSUPPORTED, "tensor too large");
+  const int64_t units = B * Hkv;
+  const int nsplit = eiat::decode_splits(units, nk);
+  if (units * nsplit > (int64_t)INT32_MAX) return fail(EIAT_ERR_UNSUPPORTED, "grid too large");
+  if (B == 0 || nq == 0) return ok();
+  float qk_scale = 1.0f;
+  int qmode = 0;
+  if (scale > 0.0f) {
+    qk_scale = (float)((double)scale * 1.4426950408889634);
+  } else if (scale < 0.0f) {
+    qmode = 1;
+    qk_scale = (float)(-(double)scale * 1.4426950408889634);
+  } else {
+    qmode = 2;
+  }
+  if (!isfinite(qk_scale)) return fail(EIAT_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+  if (!q || !k || !v || !o || !lse || !workspace)
+    return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
+  const void* ptrs[6] = {q, k, v, o, lse, workspace};
+  for (int i = 0; i < 6; ++i)
+    if (!aligned16(ptrs[i])) return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t need = attn_decode_workspace_bytes(B, H, Hkv, nq, nk, dv);
+  if (workspace_bytes < need)
+    return fail(EIAT_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  const size_t eb = elem_bytes(dtype);
+  const size_t qb = (size_t)(B * H * nq * d) * eb, kb = (size_t)(B * Hkv * nk * d) * eb;
+  const size_t ob = (size_t)(B * H * nq * dv) * eb, lb = (size_t)(B * H * nq) * 4;
+  const void* ins[3] = {q, k, v};
+  const size_t insz[3] = {qb, kb, kb};
+  void* outs[3] = {o, lse, workspace};
+  const size_t outsz[3] = {ob, lb, need};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
+        return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap inputs");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
+        return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap each other");
+  }
+
+  eiat::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = static_cast<float*>(workspace);
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.nq = nq;
+  a.nk = nk;
+  a.d = (int)d;
+  a.dtype = dtype;
+  a.mask = mask;
+  a.window = mask == EIAT_MASK_WINDOW ? (window < nk ? window : nk) : 0;
+  a.qk_scale = qk_scale;
+  a.qmode = qmode;
+  a.nsplit = nsplit;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = eiat::launch_decode(a);
+  if (e != hipSuccess) return fail(EIAT_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case EIAT_OK: return "EIAT_OK";

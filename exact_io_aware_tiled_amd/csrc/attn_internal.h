@@ -49,7 +49,30 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Decode-shaped forward: nq new rows per query head against nk cached keys.
+struct DecodeArgs {
+  const void* q;     // [B][H][nq][d]
+  const void* k;     // [B][Hkv][nk][d]
+  const void* v;     // [B][Hkv][nk][d]
+  void* o;           // [B][H][nq][d]
+  float* lse;        // [B][H][nq]
+  float* workspace;  // range summaries (attn_decode_workspace_bytes() bytes)
+  int64_t B, H, Hkv, nq, nk;
+  int d;             // == dv, 64 or 128
+  int dtype;         // 1 f16, 2 bf16
+  int mask;
+  int64_t window;    // clamped to nk
+  float qk_scale;    // as FwdArgs
+  int qmode;
+  int nsplit;        // decode_splits(B * Hkv, nk)
+  hipStream_t stream;
+};
+
+// Cache ranges per (batch, key/value head) used by the decode kernels.
+int decode_splits(int64_t units, int64_t nk);
+
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 
 }  // namespace eiat

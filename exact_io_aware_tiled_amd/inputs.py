@@ -97,3 +97,63 @@ def make_inputs(w: Workload, seed: Optional[int] = None, with_grad: bool = False
 def small(w: Workload, **kw) -> Workload:
     """A reduced copy of ``w`` (same dtype, mask and distributions) for fast checks."""
     return w.replace(**kw)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """nq new rows per query head against a cache of nk keys and values.
+
+    Q: [B, H, nq, d]; K: [B, Hkv, nk, d]; V: [B, Hkv, nk, dv]; H a multiple of Hkv.
+    The rows are the last nq of nk positions.
+    """
+
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    nq: int
+    nk: int
+    d: int
+    dv: int
+    dtype: str
+    mask: str = "none"
+    window: int = 0
+    scale: Optional[float] = None  # default 1/sqrt(d)
+    seed: int = 2000
+
+    @property
+    def c(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
+
+    def replace(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# Decode shapes.  decode_7b is the Principia page's own KV-cache example (a
+# 7B-class model: 32 heads of 128, fp16, 4096 cached tokens per session), one
+# layer for a batch of 16 sessions; the others vary the head sharing, the
+# context length and the number of new rows (a few drafted positions checked
+# in one pass).
+DECODE_WORKLOADS = {
+    "decode_7b": DecodeWorkload("decode_7b", 16, 32, 32, 1, 4096, 128, 128, "f16", seed=2001),
+    "decode_gqa": DecodeWorkload("decode_gqa", 16, 32, 8, 1, 16384, 128, 128, "bf16", seed=2002),
+    "decode_long": DecodeWorkload("decode_long", 1, 32, 8, 1, 65536, 128, 128, "bf16", seed=2003),
+    "decode_verify": DecodeWorkload("decode_verify", 16, 32, 32, 4, 4096, 128, 128, "f16",
+                                    "causal", seed=2004),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None, device="cpu") -> dict:
+    """Draw Q, K, V for a decode workload (CPU generator, float32 N(0, 1) in the
+    order Q, K, V, each rounded once to ``w.dtype``)."""
+    g = torch.Generator("cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    dt = DTYPES[w.dtype]
+    q = torch.randn((w.B, w.H, w.nq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Hkv, w.nk, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Hkv, w.nk, w.dv), generator=g, dtype=torch.float32)
+    out = {"q": q.to(dt), "k": k.to(dt), "v": v.to(dt)}
+    if device != "cpu":
+        out = {key: t.to(device) for key, t in out.items()}
+    return out
+

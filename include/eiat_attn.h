@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define EIAT_ABI_VERSION 1
+#define EIAT_ABI_VERSION 2  /* 2: adds attn_decode */
 
 /* Symbols of the shared library (built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -136,6 +136,38 @@ EIAT_API eiat_status attn_bwd_stage(int stage, const void *q, const void *k, con
                                     void *stream);
 
 /* Static string naming a status code. */
+/*
+ * Decode-shaped forward: a few new query rows per head against a long cache of
+ * keys and values (the KV-cache setting of webturing.com.tr Principia,
+ * "Bellek Duvarinin Fizigi", section on the KV cache and long context; the
+ * rows are the dense definition above, computed as the merge of the stable
+ * summaries of ranges of the cache, alphabetamath.cc Definition "Stable
+ * summary of an attention key block").
+ *
+ *   q        [B][H][nq][d]   the last nq positions of each sequence
+ *   k, v     [B][Hkv][nk][d], [B][Hkv][nk][dv]   keys and values of all nk positions
+ *   o        [B][H][nq][dv]  (dtype), lse [B][H][nq] float32, natural logarithm
+ *   workspace  device buffer of at least attn_decode_workspace_bytes(...) bytes;
+ *            overwritten (the per-range summaries), no initial contents needed
+ *
+ * Row i of q sits at position nk - nq + i; its allowed keys are the mask's set
+ * for that position (none: every cached key; causal: j <= nk - nq + i;
+ * window: the last `window` keys up to that position).  H must be a multiple of
+ * Hkv; query head h reads key/value head h / (H / Hkv) (Hkv == H: one each).
+ * Requires 1 <= nq <= nk when B > 0 (B == 0 or nq == 0 does nothing).
+ * Kernels: dtype F16 or BF16, d == dv in {64, 128}, (H / Hkv) * nq <= 32;
+ * other valid arguments return EIAT_ERR_UNSUPPORTED.  Pointers 16-byte
+ * aligned; outputs and workspace must not overlap inputs or each other.
+ * Calls sharing one workspace on different streams race.
+ */
+EIAT_API size_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t nq,
+                                            int64_t nk, int64_t dv);
+
+EIAT_API eiat_status attn_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 void *workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                                 int64_t Hkv, int64_t nq, int64_t nk, int64_t d, int64_t dv,
+                                 int dtype, float scale, int mask, int64_t window, void *stream);
+
 EIAT_API const char *attn_status_string(int status);
 
 /* Thread-local detail of the calling thread's last non-OK return ("" if none). */

@@ -17,10 +17,11 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = A.header_functions()
     assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
-                          "attn_status_string", "attn_last_error", "attn_abi_version"}
+                          "attn_decode", "attn_decode_workspace_bytes", "attn_status_string",
+                          "attn_last_error", "attn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -104,3 +105,47 @@ def test_python_binding_requires_gpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         A.attn_fwd(q, q, q)
+
+
+def dec(lib, ws_bytes=None, **kw):
+    args = dict(q=F, k=F * 2**20, v=F * 2**21, o=F * 2**22, lse=F * 2**23, ws=F * 2**24, B=2, H=8,
+                Hkv=2, nq=3, nk=100, d=64, dv=64, dtype=2, scale=0.125, mask=1, window=0)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(args["B"], args["H"], args["Hkv"], args["nq"],
+                                                   args["nk"], args["dv"])
+    return lib.attn_decode(args["q"], args["k"], args["v"], args["o"], args["lse"], args["ws"],
+                           ws_bytes, args["B"], args["H"], args["Hkv"], args["nq"], args["nk"],
+                           args["d"], args["dv"], args["dtype"], args["scale"], args["mask"],
+                           args["window"], None)
+
+
+def test_decode_workspace_bytes(lib):
+    # units * ranges * rows * (dv + 2) floats; ranges: ~2048 single-wave workgroups in all
+    assert lib.attn_decode_workspace_bytes(16, 32, 32, 1, 4096, 128) == 512 * 4 * 1 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(1, 32, 8, 1, 65536, 128) == 8 * 256 * 4 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(1, 1, 1, 1, 1, 64) == 1 * 1 * 1 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(0, 8, 2, 1, 10, 64) == 0
+    assert lib.attn_decode_workspace_bytes(1, 6, 4, 1, 10, 64) == 0  # 6 heads do not split over 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=6, Hkv=4), 1), (dict(Hkv=0), 1), (dict(nq=101), 1), (dict(nk=-1), 1),
+    (dict(mask=2, window=0), 1), (dict(dtype=5), 1), (dict(scale=float("nan")), 1),
+    (dict(q=0), 1), (dict(ws=0), 1), (dict(lse=F * 2**23 + 8), 1),
+    (dict(o=F), 1),  # overlaps q
+    (dict(ws=F * 2**22), 1),  # overlaps o
+    (dict(dtype=0), 2), (dict(d=16, dv=16), 2), (dict(d=128, dv=64), 2),
+    (dict(H=64, Hkv=2, nq=2), 2),  # 64 rows per key/value head
+])
+def test_decode_rejects(lib, kw, code):
+    assert dec(lib, **kw) == code
+    assert lib.attn_last_error() != b""
+
+
+def test_decode_small_workspace_and_empty(lib):
+    need = lib.attn_decode_workspace_bytes(2, 8, 2, 3, 100, 64)
+    assert dec(lib, ws_bytes=need - 1) == 1
+    assert b"workspace" in lib.attn_last_error()
+    assert dec(lib, B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0) == 0
+    assert dec(lib, nq=0, ws_bytes=0) == 0
