@@ -34,7 +34,9 @@ METRIC = "fwd/bwd attention TFLOP/s, n=4096 d=64 bf16 causal; % of MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip"]
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
+DECODE_METRIC = ("decode attention GB/s: algorithmic HBM bytes (Q, K, V read once, O and LSE "
+                 "written once) per second")
 
 
 def log(*a):
@@ -74,12 +76,10 @@ def load_traffic(kernel: str, workload) -> float | None:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = data.get("kernels", {}).get(kernel)
-    if not entry or data.get("sources_sha") != sources_digest():
+    if data.get("sources_sha") != sources_digest():
         return None
-    if data.get("workload") != repr(workload):
-        return None
-    return entry.get("bytes_per_launch")
+    entry = data.get("workloads", {}).get(repr(workload), {}).get("kernels", {}).get(kernel)
+    return entry.get("bytes_per_launch") if entry else None
 
 
 def cpu_baseline(w, budget_s: float):
@@ -112,6 +112,140 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def time_kernels(torch, kernels, warmup: int, steps: int, stream):
+    """Run `steps` timed steps (each: every kernel once, in order) after
+    `warmup` untimed ones; per-kernel mean ms from HIP events on `stream`,
+    and the wall-clock ms per step."""
+    def step(evs=None):
+        for i, (_, fn) in enumerate(kernels):
+            if evs is not None:
+                evs[i].record(stream)
+            fn()
+        if evs is not None:
+            evs[len(kernels)].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = {name: sum(events[s_][i].elapsed_time(events[s_][i + 1]) for s_ in range(steps)) / steps
+               for i, (name, _) in enumerate(kernels)}
+    return ms_per_step, kern_ms
+
+
+def decode_cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle's decode rows on whole key/value-head groups of batch
+    entry 0 until budget_s; rate in the metric's unit (algorithmic bytes / s)."""
+    import oracle
+    from exact_io_aware_tiled_amd.inputs import make_decode_inputs
+
+    inp = make_decode_inputs(w)
+    G = w.H // w.Hkv
+    e = 2
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    groups, t_total, nbytes = 0, 0.0, 0.0
+    for g in range(w.Hkv):
+        q = f64(inp["q"][:1, g * G:(g + 1) * G])
+        k = f64(inp["k"][:1, g:g + 1])
+        v = f64(inp["v"][:1, g:g + 1])
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, w.c, w.mask, w.window)
+        t_total += time.perf_counter() - t0
+        groups += 1
+        nbytes += (G * w.nq * (w.d + w.dv) + w.nk * (w.d + w.dv)) * e + G * w.nq * 4
+        if t_total >= budget_s:
+            break
+    return {
+        "value": nbytes / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 dense oracle decode rows, {groups} of {w.B * w.Hkv} key/value-head "
+                   f"groups (batch entry 0) of the same workload; {t_total:.2f} s"),
+    }
+
+
+def bench_decode(args, w):
+    import torch
+
+    from exact_io_aware_tiled_amd import attn
+    from exact_io_aware_tiled_amd.inputs import make_decode_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_decode_inputs(w, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o = torch.empty(w.B, w.H, w.nq, w.dv, dtype=q.dtype, device=dev)
+    lse = torch.empty(w.B, w.H, w.nq, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(attn.attn_decode_workspace_bytes(w.B, w.H, w.Hkv, w.nq, w.nk, w.dv), 16),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def stage(s_):
+        return lambda: attn.attn_decode(q, k, v, w.c, w.mask, w.window, out=o, lse=lse,
+                                        workspace=ws, stream=stream, stage=s_)
+
+    log(f"bench: decode workload {w}")
+    kernels = [("decode_split", stage(0)), ("decode_merge", stage(1))]
+    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, args.steps, stream)
+    log("bench: kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in kern_ms.items()}))
+
+    e = q.element_size()
+    q_b = w.B * w.H * w.nq * w.d * e
+    kv_b = w.B * w.Hkv * w.nk * (w.d + w.dv) * e
+    out_b = w.B * w.H * w.nq * w.dv * e + w.B * w.H * w.nq * 4
+    work = {"decode_split": q_b + kv_b, "decode_merge": out_b}
+    value = (q_b + kv_b + out_b) / (ms_per_step * 1e-3) / 1e9
+    per_kernel = {name: {"ms": round(ms, 4), "bound": "hbm",
+                         "gbs": round(work[name] / (ms * 1e-3) / 1e9, 1)}
+                  for name, ms in kern_ms.items()}
+    dom = max(kern_ms, key=kern_ms.get)
+    achieved = work[dom] / (kern_ms[dom] * 1e-3) / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(dom, w)}
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration {nbytes} bytes read, {nbytes} bytes written")
+    cpu = decode_cpu_baseline(w, args.cpu_budget) if args.cpu_budget > 0 else None
+    line = {
+        "metric": DECODE_METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V)",
+        "config": {"workload": (f"{w.name}: B={w.B} H={w.H} Hkv={w.Hkv} nq={w.nq} nk={w.nk} "
+                                f"d=v={w.d} {w.dtype} {w.mask}"),
+                   "global_batch": w.B, "seq_len": w.nk, "heads": w.H, "kv_heads": w.Hkv,
+                   "new_rows": w.nq, "head_dim": w.d, "mask": w.mask,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,9 +270,17 @@ def main():
     import torch
 
     from exact_io_aware_tiled_amd import attn
-    from exact_io_aware_tiled_amd.inputs import DTYPES, WORKLOADS, make_inputs
+    from exact_io_aware_tiled_amd.inputs import DECODE_WORKLOADS, DTYPES, WORKLOADS, make_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload in DECODE_WORKLOADS:
+        w = DECODE_WORKLOADS[args.workload]
+        for kv in args.set:
+            key, val = kv.split("=", 1)
+            cur = getattr(w, key)
+            w = w.replace(**{key: type(cur)(val) if cur is not None else float(val)})
+        bench_decode(args, w)
+        return
     w = WORKLOADS[args.workload]
     for kv in args.set:
         key, val = kv.split("=", 1)
@@ -181,32 +323,9 @@ def main():
         kernels += [("bwd_delta", lambda: bwd_stage(0)), ("bwd_dkdv", lambda: bwd_stage(1)),
                     ("bwd_dq", lambda: bwd_stage(2))]
 
-    def step(evs=None):
-        for i, (_, fn) in enumerate(kernels):
-            if evs is not None:
-                evs[i].record(stream)
-            fn()
-        if evs is not None:
-            evs[len(kernels)].record(stream)
-
     log(f"bench: workload {w}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     K = args.steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
-              for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        step(events[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-
-    kern_ms = {name: sum(events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)) / K
-               for i, (name, _) in enumerate(kernels)}
+    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream)
     log("bench: kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in kern_ms.items()}))
 
     bh = B * H

@@ -66,6 +66,8 @@ def load_library():
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64,
                                 i64, i64, c_int, c_float, c_int, i64, vp]
     lib.attn_decode.restype = c_int
+    lib.attn_decode_stage.argtypes = [c_int] + lib.attn_decode.argtypes
+    lib.attn_decode_stage.restype = c_int
     lib.attn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [c_int]
@@ -161,11 +163,13 @@ def attn_decode_workspace_bytes(B: int, H: int, Hkv: int, nq: int, nk: int, dv: 
 
 
 def attn_decode(q, k, v, scale: Optional[float] = None, mask: str = "none", window: int = 0,
-                out=None, lse=None, workspace=None, stream=None):
+                out=None, lse=None, workspace=None, stream=None, stage: Optional[int] = None):
     """O, LSE for nq new rows against a key/value cache.
 
     q: [B, H, nq, d] (the last nq positions); k: [B, Hkv, nk, d]; v: [B, Hkv, nk, dv];
     H a multiple of Hkv (query head h reads key/value head h // (H // Hkv)).
+    stage=None runs attn_decode; stage 0 / 1 runs attn_decode_stage (range
+    summaries into `workspace`; their merge into out, lse) -- pass the same workspace.
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -184,8 +188,12 @@ def attn_decode(q, k, v, scale: Optional[float] = None, mask: str = "none", wind
     ws_bytes = attn_decode_workspace_bytes(B, H, Hkv, nq, nk, dv)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    _check(lib.attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                           workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H,
-                           Hkv, nq, nk, d, dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask],
-                           int(window), _stream_handle(stream)))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, Hkv, nq, nk,
+            d, dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask], int(window),
+            _stream_handle(stream))
+    if stage is None:
+        _check(lib.attn_decode(*args))
+    else:
+        _check(lib.attn_decode_stage(int(stage), *args))
     return out, lse

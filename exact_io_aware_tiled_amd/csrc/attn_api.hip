@@ -221,10 +221,11 @@ size_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t nq
   return (size_t)units * (size_t)S * (size_t)M * (size_t)(dv + 2) * sizeof(float);
 }
 
-eiat_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
-                        int64_t Hkv, int64_t nq, int64_t nk, int64_t d, int64_t dv, int dtype,
-                        float scale, int mask, int64_t window, void* stream) {
+static eiat_status decode_impl(int stages, const void* q, const void* k, const void* v, void* o,
+                               float* lse, void* workspace, size_t workspace_bytes, int64_t B,
+                               int64_t H, int64_t Hkv, int64_t nq, int64_t nk, int64_t d,
+                               int64_t dv, int dtype, float scale, int mask, int64_t window,
+                               void* stream) {
   if (B < 0 || nq < 0 || nk < 0) return fail(EIAT_ERR_INVALID_ARG, "B, nq and nk must be >= 0");
   if (H < 1 || Hkv < 1) return fail(EIAT_ERR_INVALID_ARG, "H and Hkv must be >= 1");
   if (H % Hkv != 0)
@@ -309,10 +310,29 @@ eiat_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
   a.qk_scale = qk_scale;
   a.qmode = qmode;
   a.nsplit = nsplit;
+  a.stages = stages;
   a.stream = static_cast<hipStream_t>(stream);
   hipError_t e = eiat::launch_decode(a);
   if (e != hipSuccess) return fail(EIAT_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+eiat_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                        int64_t Hkv, int64_t nq, int64_t nk, int64_t d, int64_t dv, int dtype,
+                        float scale, int mask, int64_t window, void* stream) {
+  return decode_impl(3, q, k, v, o, lse, workspace, workspace_bytes, B, H, Hkv, nq, nk, d, dv,
+                     dtype, scale, mask, window, stream);
+}
+
+eiat_status attn_decode_stage(int stage, const void* q, const void* k, const void* v, void* o,
+                              float* lse, void* workspace, size_t workspace_bytes, int64_t B,
+                              int64_t H, int64_t Hkv, int64_t nq, int64_t nk, int64_t d,
+                              int64_t dv, int dtype, float scale, int mask, int64_t window,
+                              void* stream) {
+  if (stage < 0 || stage > 1) return fail(EIAT_ERR_INVALID_ARG, "unknown decode stage %d", stage);
+  return decode_impl(1 << stage, q, k, v, o, lse, workspace, workspace_bytes, B, H, Hkv, nq, nk,
+                     d, dv, dtype, scale, mask, window, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(64)
     attn_decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                              const T* __restrict__ V, float* __restrict__ zpart,
                              float2* __restrict__ mlpart, int H, int Hkv, int nq, int nk, int M,
-                             int units, int nsplit, int window, float qk_scale, int qmode) {
+                             int nsplit, int window, float qk_scale, int qmode) {
   using C = DecCfg<T, D>;
   constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -87,8 +87,10 @@ __global__ void __launch_bounds__(64)
   const int lane = threadIdx.x;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int unit = blockIdx.x % units;  // (b, key/value head): consecutive blocks, other heads
-  const int split = blockIdx.x / units;
+  // Consecutive workgroups take consecutive ranges of one (batch, key/value
+  // head), so the workgroups resident at once stream neighbouring memory.
+  const int unit = blockIdx.x / nsplit;
+  const int split = blockIdx.x % nsplit;
   const int b = unit / Hkv, hk = unit % Hkv;
   const int G = H / Hkv;
 
@@ -208,44 +210,85 @@ __global__ void __launch_bounds__(64)
   }
 }
 
-// Merge the nsplit range summaries of one output row, left to right, with the
-// Definition's merge (m' = max, both sides rescaled by 2^(m - m')), then
-// O = z / l and LSE = (m + log2 l) ln 2.  One wave per row of O.
+// Merge the nsplit range summaries of one output row with the Definition's
+// merge.  The merge is associative and commutative, so it is taken in one
+// step: m = max_s m_s, weights w_s = 2^(m_s - m) (0 for a range with no allowed
+// key), l = sum_s w_s l_s, z = sum_s w_s z_s; then O = z / l and
+// LSE = (m + log2 l) ln 2.  One workgroup of four waves per row of O: all
+// threads share the ranges for m, the weights (kept in LDS) and l; each wave
+// sums every output column over a quarter of the ranges (independent loads),
+// and the four partial sums are added in LDS.
+constexpr int kMaxSplits = 2048;
+constexpr int kMergeWaves = 4;
+
 template <typename T, int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(64 * kMergeWaves)
     attn_decode_combine_kernel(const float* __restrict__ zpart, const float2* __restrict__ mlpart,
                                T* __restrict__ O, float* __restrict__ LSE, int H, int Hkv, int nq,
                                int M, int nsplit) {
   constexpr int CPL = D / 64;  // output columns per lane
-  const int lane = threadIdx.x;
+  constexpr int NT = 64 * kMergeWaves;
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float zsh[kMergeWaves][D];
+  __shared__ float red[2][kMergeWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;  // ((b * H + hq) * nq + i): the row of O and LSE
   const int i = row % nq, bh = row / nq;
   const int hq = bh % H, b = bh / H;
   const int G = H / Hkv;
   const int unit = b * Hkv + hq / G;
   const int r = (hq % G) * nq + i;
+  const int64_t base = (int64_t)unit * nsplit * M + r;  // summary row of range s: base + s * M
 
-  float m = -INFINITY, l = 0.0f, z[CPL];
+  float m = -INFINITY;
+  for (int s = tid; s < nsplit; s += NT) m = fmaxf(m, mlpart[base + (int64_t)s * M].x);
+  m = wave_max(m);
+  if (lane == 0) red[0][wave] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) m = fmaxf(m, red[0][w]);
+  float l = 0.0f;
+  for (int s = tid; s < nsplit; s += NT) {
+    const float2 ml = mlpart[base + (int64_t)s * M];
+    const float w = (ml.x == -INFINITY) ? 0.0f : fast_exp2(ml.x - m);
+    wsh[s] = w;
+    l += w * ml.y;
+  }
+  l = wave_sum(l);
+  if (lane == 0) red[1][wave] = l;
+  __syncthreads();
+
+  float z[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) z[k] = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t prow = ((int64_t)unit * nsplit + s) * M + r;
-    const float2 ml = mlpart[prow];
-    if (ml.x == -INFINITY) continue;  // no allowed key of this row in that range
-    const float mn = fmaxf(m, ml.x);
-    const float a = fast_exp2(m - mn), bs = fast_exp2(ml.x - mn);
-    l = l * a + ml.y * bs;
-    const float* zr = zpart + prow * D + lane * CPL;
+  const float* zr = zpart + base * D + lane * CPL;
+#pragma unroll 8
+  for (int s = wave; s < nsplit; s += kMergeWaves) {
+    const float w = wsh[s];
+    const float* zs = zr + (int64_t)s * M * D;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) z[k] = z[k] * a + zr[k] * bs;
-    m = mn;
+    for (int k = 0; k < CPL; ++k) z[k] += w * zs[k];
   }
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) zsh[wave][lane * CPL + k] = z[k];
+  __syncthreads();
+  if (wave != 0) return;
+  l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) l += red[1][w];
   const float inv = 1.0f / l;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) acc += zsh[w][lane * CPL + k];
+    z[k] = acc * inv;
+  }
   T* orow = O + (int64_t)row * D + lane * CPL;
   if constexpr (CPL == 2) {
-    *reinterpret_cast<uint32_t*>(orow) = Elt<T>::pack2(z[0] * inv, z[1] * inv);
+    *reinterpret_cast<uint32_t*>(orow) = Elt<T>::pack2(z[0], z[1]);
   } else {
-    orow[0] = static_cast<T>(z[0] * inv);
+    orow[0] = static_cast<T>(z[0]);
   }
   if (lane == 0) LSE[row] = (m + fast_log2(l)) * kLn2;
 }
@@ -259,6 +302,7 @@ int decode_splits(int64_t units, int64_t nk) {
   int64_t s = (2048 + units - 1) / units;
   if (s > tiles) s = tiles;
   if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
   const int64_t per = (tiles + s - 1) / s;
   return (int)((tiles + per - 1) / per);
 }
@@ -269,17 +313,22 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int M = (int)(a.H / a.Hkv * a.nq);
   float* zpart = a.workspace;
   float2* mlpart = reinterpret_cast<float2*>(a.workspace + (int64_t)units * a.nsplit * M * D);
-  hipLaunchKernelGGL((attn_decode_split_kernel<T, D, MASK>), dim3((unsigned)(units * a.nsplit)),
-                     dim3(64), 0, a.stream, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), zpart, mlpart,
-                     (int)a.H, (int)a.Hkv, (int)a.nq, (int)a.nk, M, units, a.nsplit,
-                     (int)a.window, a.qk_scale, a.qmode);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_combine_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.nq)),
-                     dim3(64), 0, a.stream, zpart, mlpart, static_cast<T*>(a.o), a.lse, (int)a.H,
-                     (int)a.Hkv, (int)a.nq, M, a.nsplit);
-  return hipGetLastError();
+  if (a.stages & 1) {
+    hipLaunchKernelGGL((attn_decode_split_kernel<T, D, MASK>),
+                       dim3((unsigned)(units * a.nsplit)), dim3(64), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), zpart, mlpart, (int)a.H, (int)a.Hkv, (int)a.nq,
+                       (int)a.nk, M, a.nsplit, (int)a.window, a.qk_scale, a.qmode);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.stages & 2) {
+    hipLaunchKernelGGL((attn_decode_combine_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.nq)),
+                       dim3(64 * kMergeWaves), 0, a.stream, zpart, mlpart, static_cast<T*>(a.o), a.lse,
+                       (int)a.H, (int)a.Hkv, (int)a.nq, M, a.nsplit);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <typename T, int D>

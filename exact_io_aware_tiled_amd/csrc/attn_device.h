@@ -315,6 +315,18 @@ __device__ inline float tile_max(const f32x16 (&s)[NSB]) {
 // True in every lane when `pred` holds in at least one lane of the wave.
 __device__ inline bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
+// Maximum / sum of x over the 64 lanes of the wave (result in every lane).
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return halves_max(x);
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, 64);
+  return halves_sum(x);
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -65,6 +65,7 @@ struct DecodeArgs {
   float qk_scale;    // as FwdArgs
   int qmode;
   int nsplit;        // decode_splits(B * Hkv, nk)
+  int stages;        // bit 0: range summaries, bit 1: merge into O and LSE
   hipStream_t stream;
 };
 

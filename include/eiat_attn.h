@@ -168,6 +168,19 @@ EIAT_API eiat_status attn_decode(const void *q, const void *k, const void *v, vo
                                  int64_t Hkv, int64_t nq, int64_t nk, int64_t d, int64_t dv,
                                  int dtype, float scale, int mask, int64_t window, void *stream);
 
+/*
+ * One step of attn_decode, for callers that schedule or time the steps
+ * separately: stage 0 writes the summaries of the cache ranges into
+ * `workspace`; stage 1 merges them into o and lse.  Same arguments and checks
+ * as attn_decode (stage 1 reads the workspace stage 0 wrote for the same
+ * shapes); an unknown stage returns EIAT_ERR_INVALID_ARG.
+ */
+EIAT_API eiat_status attn_decode_stage(int stage, const void *q, const void *k, const void *v,
+                                       void *o, float *lse, void *workspace,
+                                       size_t workspace_bytes, int64_t B, int64_t H, int64_t Hkv,
+                                       int64_t nq, int64_t nk, int64_t d, int64_t dv, int dtype,
+                                       float scale, int mask, int64_t window, void *stream);
+
 EIAT_API const char *attn_status_string(int status);
 
 /* Thread-local detail of the calling thread's last non-OK return ("" if none). */

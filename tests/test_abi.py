@@ -17,7 +17,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = A.header_functions()
     assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
-                          "attn_decode", "attn_decode_workspace_bytes", "attn_status_string",
+                          "attn_decode", "attn_decode_stage", "attn_decode_workspace_bytes",
+                          "attn_status_string",
                           "attn_last_error", "attn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -149,3 +150,13 @@ def test_decode_small_workspace_and_empty(lib):
     assert b"workspace" in lib.attn_last_error()
     assert dec(lib, B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0) == 0
     assert dec(lib, nq=0, ws_bytes=0) == 0
+
+
+def test_decode_stage_rejects_unknown_stage(lib):
+    need = lib.attn_decode_workspace_bytes(2, 8, 2, 3, 100, 64)
+    args = [F, F * 2**20, F * 2**21, F * 2**22, F * 2**23, F * 2**24, need, 2, 8, 2, 3, 100, 64,
+            64, 2, 0.125, 1, 0, None]
+    assert lib.attn_decode_stage(2, *args) == 1
+    assert lib.attn_decode_stage(-1, *args) == 1
+    assert b"stage" in lib.attn_last_error()
+

@@ -114,3 +114,15 @@ def test_decode_deterministic():
     _, o1, l1 = run(w)
     _, o2, l2 = run(w)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_stages_equal_one_call():
+    """attn_decode_stage 0 then 1 (the benchmark's timed steps) == attn_decode."""
+    w = DECODE_WORKLOADS["decode_verify"].replace(B=2, nk=1500)
+    inp, o, lse = run(w)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    o2, l2 = attn_decode(q, k, v, w.c, w.mask, w.window, workspace=ws, stage=0)
+    o2, l2 = attn_decode(q, k, v, w.c, w.mask, w.window, out=o2, lse=l2, workspace=ws, stage=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
