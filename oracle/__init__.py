@@ -73,6 +73,19 @@ def _load():
         lib.oracle_decode.argtypes = [i64, i64, i64, i64, i64, i64, i64, ip, ip, ip, dbl,
                                       ctypes.c_int, i64, ip, ip]
         lib.oracle_decode.restype = ctypes.c_int
+        u64 = ctypes.c_uint64
+        lib.oracle_fwd_drop.argtypes = [i64, i64, i64, i64, ip, ip, ip, dbl, ctypes.c_int, i64,
+                                        u64, ctypes.c_int, ip, ip]
+        lib.oracle_fwd_drop.restype = ctypes.c_int
+        lib.oracle_bwd_drop.argtypes = [i64, i64, i64, i64, ip, ip, ip, ip, dbl, ctypes.c_int,
+                                        i64, u64, ctypes.c_int, ip, ip, ip, ip, ip, ip]
+        lib.oracle_bwd_drop.restype = ctypes.c_int
+        lib.oracle_dropout_keep.argtypes = [u64, ctypes.c_int, i64, i64, i64,
+                                            ctypes.POINTER(ctypes.c_int)]
+        lib.oracle_dropout_keep.restype = ctypes.c_int
+        lib.oracle_xxh32_words.argtypes = [ip, ctypes.c_int, ctypes.c_uint32,
+                                           ctypes.POINTER(ctypes.c_uint32)]
+        lib.oracle_xxh32_words.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -137,6 +150,59 @@ def decode(q, k, v, scale: float, mask="none", window: int = 0):
     _check(lib.oracle_decode(B, H, Hkv, nq, nk, d, dv, _ptr(q), _ptr(k), _ptr(v), float(scale),
                              _mask_code(mask), int(window), _ptr(y), _ptr(lse)), "decode")
     return y, lse
+
+
+def xxh32_words(words, seed: int) -> int:
+    """XXH32 of the little-endian 32-bit words (at most 3) with a 32-bit seed."""
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
+    out = ctypes.c_uint32()
+    _check(_load().oracle_xxh32_words(_ptr(w), len(w), seed & 0xFFFFFFFF, ctypes.byref(out)),
+           "xxh32")
+    return out.value
+
+
+def dropout_keep(seed: int, thr: int, bh: int, i: int, j: int) -> bool:
+    """keep_ij of the realized dropout mask (seed, drop threshold thr / 256)."""
+    out = ctypes.c_int()
+    _check(_load().oracle_dropout_keep(seed, thr, bh, i, j, ctypes.byref(out)), "dropout_keep")
+    return bool(out.value)
+
+
+def fwd_drop(q, k, v, scale: float, mask="none", window: int = 0, seed: int = 0, thr: int = 0):
+    """Dense forward with dropout on the weights; q, k, v [..., n, d]; the flat
+    leading index is the head index bh of the mask.  Returns (Y, LSE)."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2:]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if lead else 1
+    y = np.empty((nh, n, dv))
+    lse = np.empty((nh, n))
+    _check(lib.oracle_fwd_drop(nh, n, d, dv, _ptr(q), _ptr(k), _ptr(v), float(scale),
+                               _mask_code(mask), int(window), seed, thr, _ptr(y), _ptr(lse)),
+           "fwd_drop")
+    return y.reshape(lead + (n, dv)), lse.reshape(lead + (n,))
+
+
+def bwd_drop(q, k, v, g, scale: float, mask="none", window: int = 0, seed: int = 0, thr: int = 0):
+    """VJP of sum(G * Y) for the forward with dropout (same mask replayed).
+    Returns (dQ, dK, dV, Y, delta, LSE)."""
+    lib = _load()
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2:]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if lead else 1
+    dq, dk = np.empty((nh, n, d)), np.empty((nh, n, d))
+    dvv, y = np.empty((nh, n, dv)), np.empty((nh, n, dv))
+    delta, lse = np.empty((nh, n)), np.empty((nh, n))
+    _check(lib.oracle_bwd_drop(nh, n, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
+                               _mask_code(mask), int(window), seed, thr, _ptr(dq), _ptr(dk),
+                               _ptr(dvv), _ptr(y), _ptr(delta), _ptr(lse)), "bwd_drop")
+    sh = lead + (n,)
+    return (dq.reshape(sh + (d,)), dk.reshape(sh + (d,)), dvv.reshape(sh + (dv,)),
+            y.reshape(sh + (dv,)), delta.reshape(sh), lse.reshape(sh))
 
 
 def bwd(q, k, v, g, scale: float, mask="none", window: int = 0):

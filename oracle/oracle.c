@@ -67,17 +67,93 @@ static double score(const double *qi, const double *kj, int64_t d, double c)
 }
 
 /*
+ * Dropout on the attention weights (an extension: [AM] Algorithm, reverse
+ * procedure, and Remark on rounding: the base algorithm has none, and an
+ * extension must replay the same realized mask in its reverse pass).  Reading:
+ * inverted dropout on the normalized weights, Y_i = sum_j p_ij D_ij V_j with
+ * D_ij = keep_ij * 256 / (256 - thr), the statistics m_i, l_i (and LSE) those
+ * of the undropped softmax.  The realized mask is a function of the indices,
+ * so the reverse pass regenerates it:
+ *   row key   r_i    = XXH32(le32(seed_hi) | le32(bh) | le32(i), seed_lo)
+ *   group     u_ij   = XXH32(le32(j >> 2), r_i)
+ *   keep_ij          = byte (j & 3) of u_ij (little-endian) >= thr
+ * with XXH32 the 32-bit xxHash function (its published specification, short
+ * inputs) and thr in 0..255 (drop probability thr / 256).  bh is the flat head
+ * index b * H + h.
+ */
+typedef struct {
+    uint64_t seed;
+    int thr;
+} drop_t;
+
+static uint32_t rotl32(uint32_t x, int r) { return (x << r) | (x >> (32 - r)); }
+
+/* XXH32 of a message of nwords (< 4) little-endian 32-bit words. */
+static uint32_t xxh32_words(const uint32_t *w, int nwords, uint32_t seed)
+{
+    const uint32_t P1 = 0x9E3779B1u, P2 = 0x85EBCA77u, P3 = 0xC2B2AE3Du, P4 = 0x27D4EB2Fu,
+                   P5 = 0x165667B1u;
+    (void)P1;
+    uint32_t h = seed + P5 + (uint32_t)(4 * nwords);
+    for (int k = 0; k < nwords; k++) {
+        h += w[k] * P3;
+        h = rotl32(h, 17) * P4;
+    }
+    h ^= h >> 15;
+    h *= P2;
+    h ^= h >> 13;
+    h *= P3;
+    h ^= h >> 16;
+    return h;
+}
+
+static uint32_t drop_row_key(const drop_t *dr, int64_t bh, int64_t i)
+{
+    const uint32_t w[3] = {(uint32_t)(dr->seed >> 32), (uint32_t)bh, (uint32_t)i};
+    return xxh32_words(w, 3, (uint32_t)dr->seed);
+}
+
+/* D_ij: 0 for a dropped weight, 256 / (256 - thr) for a kept one. */
+static double drop_factor(const drop_t *dr, uint32_t row_key, int64_t j)
+{
+    if (dr == NULL) return 1.0;
+    const uint32_t g = (uint32_t)(j >> 2);
+    const uint32_t u = xxh32_words(&g, 1, row_key);
+    const int byte = (int)((u >> (8 * (j & 3))) & 0xFFu);
+    return byte >= dr->thr ? 256.0 / (256.0 - dr->thr) : 0.0;
+}
+
+int oracle_xxh32_words(const uint32_t *w, int nwords, uint32_t seed, uint32_t *out)
+{
+    if (nwords < 0 || nwords > 3) return OR_EINVAL;
+    *out = xxh32_words(w, nwords, seed);
+    return OR_OK;
+}
+
+/* keep_ij of the mask above (1 kept, 0 dropped). */
+int oracle_dropout_keep(uint64_t seed, int thr, int64_t bh, int64_t i, int64_t j, int *keep)
+{
+    if (thr < 0 || thr > 255 || bh < 0 || i < 0 || j < 0) return OR_EINVAL;
+    drop_t dr = {seed, thr};
+    *keep = drop_factor(&dr, drop_row_key(&dr, bh, i), j) != 0.0;
+    return OR_OK;
+}
+
+/*
  * One row of the dense definition ([AM] Theorem "Tiled attention ... are exact",
  * the displayed dense masked attention row, with the max shift of step 2.1):
  *   m_i = max_{j in A_i} s_ij,  l_i = sum_{j in A_i} e^{s_ij - m_i},
  *   Y_i = sum_{j in A_i} (e^{s_ij - m_i} / l_i) V_j,
  * for the query vector qi sitting at row position i (A_i is the mask's set for
- * position i over keys 0..n-1).  srow is caller scratch of length n.
+ * position i over keys 0..n-1), with the dropout factors D_ij in the value sum
+ * when dr != NULL (head bh).  srow is caller scratch of length n.
  */
 static void dense_row_at(const double *qi, const double *K, const double *V, int64_t n,
                          int64_t d, int64_t dv, double c, int mask, int64_t window, int64_t i,
-                         double *srow, double *y, double *m_out, double *l_out)
+                         const drop_t *dr, int64_t bh, double *srow, double *y, double *m_out,
+                         double *l_out)
 {
+    const uint32_t rk = dr ? drop_row_key(dr, bh, i) : 0u;
     double m = -INFINITY;
     for (int64_t j = 0; j < n; j++) {
         if (!in_allowed(mask, window, i, j)) continue;
@@ -92,7 +168,7 @@ static void dense_row_at(const double *qi, const double *K, const double *V, int
     for (int64_t a = 0; a < dv; a++) y[a] = 0.0;
     for (int64_t j = 0; j < n; j++) {
         if (!in_allowed(mask, window, i, j)) continue;
-        double p = exp(srow[j] - m) / l;
+        double p = exp(srow[j] - m) / l * drop_factor(dr, rk, j);
         const double *vj = V + j * dv;
         for (int64_t a = 0; a < dv; a++) y[a] += p * vj[a];
     }
@@ -102,10 +178,11 @@ static void dense_row_at(const double *qi, const double *K, const double *V, int
 
 /* Row i of the dense definition with its own query vector Q_i. */
 static void dense_row(const double *Q, const double *K, const double *V, int64_t n, int64_t d,
-                      int64_t dv, double c, int mask, int64_t window, int64_t i, double *srow,
-                      double *y, double *m_out, double *l_out)
+                      int64_t dv, double c, int mask, int64_t window, int64_t i,
+                      const drop_t *dr, int64_t bh, double *srow, double *y, double *m_out,
+                      double *l_out)
 {
-    dense_row_at(Q + i * d, K, V, n, d, dv, c, mask, window, i, srow, y, m_out, l_out);
+    dense_row_at(Q + i * d, K, V, n, d, dv, c, mask, window, i, dr, bh, srow, y, m_out, l_out);
 }
 
 /*
@@ -115,9 +192,10 @@ static void dense_row(const double *Q, const double *K, const double *V, int64_t
  * for M (row max), L (normaliser l) and LSE = m + ln l (natural log).
  * Any of M, L, LSE may be NULL.
  */
-int oracle_fwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, const double *K,
-               const double *V, double c, int mask, int64_t window, const int64_t *rows,
-               int64_t nrows, double *Y, double *M, double *L, double *LSE)
+static int fwd_core(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q,
+                    const double *K, const double *V, double c, int mask, int64_t window,
+                    const drop_t *dr, const int64_t *rows, int64_t nrows, double *Y, double *M,
+                    double *L, double *LSE)
 {
     if (check_args(nh, n, d, dv, mask, window)) return OR_EINVAL;
     if (rows == NULL) nrows = n;
@@ -138,7 +216,7 @@ int oracle_fwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
                 int64_t i = rows ? rows[r] : r;
                 const double *Qh = Q + h * n * d, *Kh = K + h * n * d, *Vh = V + h * n * dv;
                 double m, l;
-                dense_row(Qh, Kh, Vh, n, d, dv, c, mask, window, i, srow,
+                dense_row(Qh, Kh, Vh, n, d, dv, c, mask, window, i, dr, h, srow,
                           Y + (h * nrows + r) * dv, &m, &l);
                 if (M) M[h * nrows + r] = m;
                 if (L) L[h * nrows + r] = l;
@@ -148,6 +226,23 @@ int oracle_fwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
         free(srow);
     }
     return failed ? OR_ENOMEM : OR_OK;
+}
+
+int oracle_fwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, const double *K,
+               const double *V, double c, int mask, int64_t window, const int64_t *rows,
+               int64_t nrows, double *Y, double *M, double *L, double *LSE)
+{
+    return fwd_core(nh, n, d, dv, Q, K, V, c, mask, window, NULL, rows, nrows, Y, M, L, LSE);
+}
+
+/* The dense forward with the dropout above (head h of nh is bh = h). */
+int oracle_fwd_drop(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q,
+                    const double *K, const double *V, double c, int mask, int64_t window,
+                    uint64_t seed, int thr, double *Y, double *LSE)
+{
+    if (thr < 0 || thr > 255) return OR_EINVAL;
+    drop_t dr = {seed, thr};
+    return fwd_core(nh, n, d, dv, Q, K, V, c, mask, window, &dr, NULL, n, Y, NULL, NULL, LSE);
 }
 
 /*
@@ -189,8 +284,8 @@ int oracle_decode(int64_t B, int64_t H, int64_t Hkv, int64_t nq, int64_t nk, int
                     const double *Vh = V + (b * Hkv + hk) * nk * dv;
                     const int64_t row = (b * H + h) * nq + i;
                     double m, l;
-                    dense_row_at(qi, Kh, Vh, nk, d, dv, c, mask, window, nk - nq + i, srow,
-                                 Y + row * dv, &m, &l);
+                    dense_row_at(qi, Kh, Vh, nk, d, dv, c, mask, window, nk - nq + i, NULL, 0,
+                                 srow, Y + row * dv, &m, &l);
                     if (LSE) LSE[row] = m + log(l);
                 }
             }
@@ -212,9 +307,10 @@ int oracle_decode(int64_t B, int64_t H, int64_t Hkv, int64_t nq, int64_t nk, int
  * Y, M, L come from the dense forward above.  Optional outputs Yout [nh][n][dv],
  * Dout (delta) and LSEout [nh][n] may be NULL.
  */
-int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, const double *K,
-               const double *V, const double *G, double c, int mask, int64_t window, double *dQ,
-               double *dK, double *dV, double *Yout, double *Dout, double *LSEout)
+static int bwd_core(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q,
+                    const double *K, const double *V, const double *G, double c, int mask,
+                    int64_t window, const drop_t *dr, double *dQ, double *dK, double *dV,
+                    double *Yout, double *Dout, double *LSEout)
 {
     if (check_args(nh, n, d, dv, mask, window)) return OR_EINVAL;
     size_t rows_total = (size_t)(nh * n);
@@ -226,7 +322,7 @@ int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
         free(Y); free(M); free(L); free(D);
         return OR_ENOMEM;
     }
-    int rc = oracle_fwd(nh, n, d, dv, Q, K, V, c, mask, window, NULL, n, Y, M, L, NULL);
+    int rc = fwd_core(nh, n, d, dv, Q, K, V, c, mask, window, dr, NULL, n, Y, M, L, NULL);
     if (rc) {
         free(Y); free(M); free(L); free(D);
         return rc;
@@ -247,6 +343,7 @@ int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
             const double *Qh = Q + h * n * d, *Kh = K + h * n * d, *Vh = V + h * n * dv;
             const double *gi = G + (h * n + i) * dv;
             double m = M[h * n + i], l = L[h * n + i], delta = D[h * n + i];
+            const uint32_t rk = dr ? drop_row_key(dr, h, i) : 0u;
             double *dqi = dQ + (h * n + i) * d;
             for (int64_t r = 0; r < d; r++) dqi[r] = 0.0;
             for (int64_t j = 0; j < n; j++) {
@@ -254,7 +351,7 @@ int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
                 double p = exp(score(Qh + i * d, Kh + j * d, d, c) - m) / l;
                 double gv = 0.0;
                 for (int64_t a = 0; a < dv; a++) gv += gi[a] * Vh[j * dv + a];
-                double gamma = p * (gv - delta);
+                double gamma = p * (drop_factor(dr, rk, j) * gv - delta);
                 for (int64_t r = 0; r < d; r++) dqi[r] += c * gamma * Kh[j * d + r];
             }
         }
@@ -274,11 +371,12 @@ int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
                 const double *gi = G + (h * n + i) * dv;
                 double m = M[h * n + i], l = L[h * n + i], delta = D[h * n + i];
                 double p = exp(score(Qh + i * d, Kh + j * d, d, c) - m) / l;
+                const double dij = dr ? drop_factor(dr, drop_row_key(dr, h, i), j) : 1.0;
                 double gv = 0.0;
                 for (int64_t a = 0; a < dv; a++) gv += gi[a] * Vh[j * dv + a];
-                double gamma = p * (gv - delta);
+                double gamma = p * (dij * gv - delta);
                 for (int64_t r = 0; r < d; r++) dkj[r] += c * gamma * Qh[i * d + r];
-                for (int64_t a = 0; a < dv; a++) dvj[a] += p * gi[a];
+                for (int64_t a = 0; a < dv; a++) dvj[a] += p * dij * gi[a];
             }
         }
     }
@@ -289,6 +387,33 @@ int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
         for (size_t t = 0; t < rows_total; t++) LSEout[t] = M[t] + log(L[t]);
     free(Y); free(M); free(L); free(D);
     return OR_OK;
+}
+
+int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, const double *K,
+               const double *V, const double *G, double c, int mask, int64_t window, double *dQ,
+               double *dK, double *dV, double *Yout, double *Dout, double *LSEout)
+{
+    return bwd_core(nh, n, d, dv, Q, K, V, G, c, mask, window, NULL, dQ, dK, dV, Yout, Dout,
+                    LSEout);
+}
+
+/*
+ * VJP of Phi = sum G * Y for the forward with dropout, the same realized mask
+ * replayed ([AM]'s requirement): with D_ij the factors above,
+ *   delta_i  = sum_a G_ia Y_ia                 (Y with dropout)
+ *   gamma_ij = p_ij (D_ij sum_a G_ia V_ja - delta_i)
+ *   dQ_i = c sum_j gamma_ij K_j,  dK_j = c sum_i gamma_ij Q_i,
+ *   dV_j = sum_i p_ij D_ij G_i.
+ */
+int oracle_bwd_drop(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q,
+                    const double *K, const double *V, const double *G, double c, int mask,
+                    int64_t window, uint64_t seed, int thr, double *dQ, double *dK, double *dV,
+                    double *Yout, double *Dout, double *LSEout)
+{
+    if (thr < 0 || thr > 255) return OR_EINVAL;
+    drop_t dr = {seed, thr};
+    return bwd_core(nh, n, d, dv, Q, K, V, G, c, mask, window, &dr, dQ, dK, dV, Yout, Dout,
+                    LSEout);
 }
 
 /*
