@@ -61,6 +61,12 @@ def load_library():
     lib.attn_bwd.restype = c_int
     lib.attn_bwd_stage.argtypes = [c_int] + lib.attn_bwd.argtypes
     lib.attn_bwd_stage.restype = c_int
+    lib.attn_fwd_dropout.argtypes = lib.attn_fwd.argtypes[:-1] + [c_float, ctypes.c_uint64, vp]
+    lib.attn_fwd_dropout.restype = c_int
+    lib.attn_bwd_dropout.argtypes = lib.attn_bwd.argtypes[:-1] + [c_float, ctypes.c_uint64, vp]
+    lib.attn_bwd_dropout.restype = c_int
+    lib.attn_bwd_dropout_stage.argtypes = [c_int] + lib.attn_bwd_dropout.argtypes
+    lib.attn_bwd_dropout_stage.restype = c_int
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64,
@@ -105,8 +111,10 @@ def _require(t: torch.Tensor, name: str):
 
 
 def attn_fwd(q, k, v, scale: Optional[float] = None, mask: str = "causal", window: int = 0,
-             out=None, lse=None, stream=None):
-    """O, LSE = attention forward.  q, k: [B, H, n, d]; v: [B, H, n, dv] (same dtype)."""
+             out=None, lse=None, stream=None, p_drop: float = 0.0, seed: int = 0):
+    """O, LSE = attention forward.  q, k: [B, H, n, d]; v: [B, H, n, dv] (same dtype).
+
+    p_drop > 0 applies dropout to the weights (attn_fwd_dropout; mask keyed on seed)."""
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require(t, name)
@@ -117,9 +125,12 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, mask: str = "causal", windo
         out = torch.empty(B, H, n, dv, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
-    _check(lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, H, n, d, dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask],
-                        int(window), _stream_handle(stream)))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n, d,
+            dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask], int(window))
+    if p_drop:
+        _check(lib.attn_fwd_dropout(*args, float(p_drop), int(seed), _stream_handle(stream)))
+    else:
+        _check(lib.attn_fwd(*args, _stream_handle(stream)))
     return out, lse
 
 
@@ -129,11 +140,12 @@ def attn_bwd_workspace_bytes(B: int, H: int, n: int) -> int:
 
 def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "causal",
              window: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None,
-             stage: Optional[int] = None):
+             stage: Optional[int] = None, p_drop: float = 0.0, seed: int = 0):
     """dQ, dK, dV of sum(dO * O) given the forward's O and LSE.
 
     stage=None runs attn_bwd (all steps); stage 0, 1 or 2 runs attn_bwd_stage
     (delta into `workspace`; dK and dV; dQ) -- pass the same workspace to all.
+    p_drop > 0 replays the dropout of attn_fwd(..., p_drop, seed) (same values).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do)):
@@ -150,11 +162,18 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "ca
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), B, H, n, d, dvd, DTYPE_CODES[q.dtype],
-            float(scale), MASK_CODES[mask], int(window), _stream_handle(stream))
-    if stage is None:
-        _check(lib.attn_bwd(*args))
+            float(scale), MASK_CODES[mask], int(window))
+    sh = _stream_handle(stream)
+    if p_drop:
+        extra = (float(p_drop), int(seed), sh)
+        if stage is None:
+            _check(lib.attn_bwd_dropout(*args, *extra))
+        else:
+            _check(lib.attn_bwd_dropout_stage(int(stage), *args, *extra))
+    elif stage is None:
+        _check(lib.attn_bwd(*args, sh))
     else:
-        _check(lib.attn_bwd_stage(int(stage), *args))
+        _check(lib.attn_bwd_stage(int(stage), *args, sh))
     return dq, dk, dv
 
 

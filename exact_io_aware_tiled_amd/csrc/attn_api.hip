@@ -78,13 +78,27 @@ eiat_status check_common(int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
   return EIAT_OK;
 }
 
+// Dropout probability -> mask threshold (drop probability thr / 256).
+eiat_status drop_params(float p_drop, uint64_t seed, eiat::DropParams* dp) {
+  if (!(p_drop >= 0.0f && p_drop < 1.0f))
+    return fail(EIAT_ERR_INVALID_ARG, "p_drop must be in [0, 1) (got %g)", (double)p_drop);
+  long thr = lrintf(p_drop * 256.0f);
+  if (thr > 255) thr = 255;
+  dp->seed_lo = (uint32_t)seed;
+  dp->seed_hi = (uint32_t)(seed >> 32);
+  dp->thr = (int)thr;
+  dp->inv_keep = (float)(256.0 / (256.0 - (double)thr));
+  return EIAT_OK;
+}
+
+const eiat::DropParams kNoDrop = {0u, 0u, 0, 1.0f};
+
 }  // namespace
 
-extern "C" {
-
-eiat_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                     int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale, int mask,
-                     int64_t window, void* stream) {
+static eiat_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int dtype,
+                            float scale, int mask, int64_t window, const eiat::DropParams& drop,
+                            void* stream) {
   bool empty = false;
   float qk_scale = 1.0f;
   int qmode = 0;
@@ -120,10 +134,29 @@ eiat_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   a.window = win;
   a.qk_scale = qk_scale;
   a.qmode = qmode;
+  a.drop = drop;
   a.stream = static_cast<hipStream_t>(stream);
   hipError_t e = eiat::launch_fwd(a);
   if (e != hipSuccess) return fail(EIAT_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+extern "C" {
+
+eiat_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale, int mask,
+                     int64_t window, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, n, d, dv, dtype, scale, mask, window, kNoDrop, stream);
+}
+
+eiat_status attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int dtype,
+                             float scale, int mask, int64_t window, float p_drop, uint64_t seed,
+                             void* stream) {
+  eiat::DropParams dp;
+  eiat_status s = drop_params(p_drop, seed, &dp);
+  if (s != EIAT_OK) return s;
+  return fwd_impl(q, k, v, o, lse, B, H, n, d, dv, dtype, scale, mask, window, dp, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n) {
@@ -135,7 +168,8 @@ static eiat_status bwd_impl(int stages, const void* q, const void* k, const void
                             const void* o, const void* dout, const float* lse, void* dq, void* dk,
                             void* dvv, void* workspace, size_t workspace_bytes, int64_t B,
                             int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale,
-                            int mask, int64_t window, void* stream) {
+                            int mask, int64_t window, const eiat::DropParams& drop,
+                            void* stream) {
   bool empty = false;
   float qk_scale = 1.0f;
   int qmode = 0;
@@ -189,6 +223,7 @@ static eiat_status bwd_impl(int stages, const void* q, const void* k, const void
   a.qmode = qmode;
   a.scale = scale;
   a.stages = stages;
+  a.drop = drop;
   a.stream = static_cast<hipStream_t>(stream);
   hipError_t e = eiat::launch_bwd(a);
   if (e != hipSuccess) return fail(EIAT_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
@@ -200,7 +235,33 @@ eiat_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      size_t workspace_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
                      int64_t dv, int dtype, float scale, int mask, int64_t window, void* stream) {
   return bwd_impl(7, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H, n, d,
-                  dv, dtype, scale, mask, window, stream);
+                  dv, dtype, scale, mask, window, kNoDrop, stream);
+}
+
+eiat_status attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dvv,
+                             void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                             int64_t n, int64_t d, int64_t dv, int dtype, float scale, int mask,
+                             int64_t window, float p_drop, uint64_t seed, void* stream) {
+  eiat::DropParams dp;
+  eiat_status s = drop_params(p_drop, seed, &dp);
+  if (s != EIAT_OK) return s;
+  return bwd_impl(7, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H, n, d,
+                  dv, dtype, scale, mask, window, dp, stream);
+}
+
+eiat_status attn_bwd_dropout_stage(int stage, const void* q, const void* k, const void* v,
+                                   const void* o, const void* dout, const float* lse, void* dq,
+                                   void* dk, void* dvv, void* workspace, size_t workspace_bytes,
+                                   int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                                   int dtype, float scale, int mask, int64_t window, float p_drop,
+                                   uint64_t seed, void* stream) {
+  if (stage < 0 || stage > 2) return fail(EIAT_ERR_INVALID_ARG, "unknown backward stage %d", stage);
+  eiat::DropParams dp;
+  eiat_status s = drop_params(p_drop, seed, &dp);
+  if (s != EIAT_OK) return s;
+  return bwd_impl(1 << stage, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H,
+                  n, d, dv, dtype, scale, mask, window, dp, stream);
 }
 
 eiat_status attn_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -210,7 +271,7 @@ eiat_status attn_bwd_stage(int stage, const void* q, const void* k, const void* 
                            int64_t window, void* stream) {
   if (stage < 0 || stage > 2) return fail(EIAT_ERR_INVALID_ARG, "unknown backward stage %d", stage);
   return bwd_impl(1 << stage, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H,
-                  n, d, dv, dtype, scale, mask, window, stream);
+                  n, d, dv, dtype, scale, mask, window, kNoDrop, stream);
 }
 
 size_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t nq, int64_t nk,

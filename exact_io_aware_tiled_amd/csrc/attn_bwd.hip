@@ -164,7 +164,8 @@ struct DkvCfg {
   static constexpr int OT = ON + BMQ * NROW;
   static constexpr int LS = OT + TBYTES;             // LSE * log2(e), BMQ floats
   static constexpr int DL = LS + BMQ * 4;            // delta, BMQ floats
-  static constexpr int BUF = DL + BMQ * 4;
+  static constexpr int RK = DL + BMQ * 4;            // dropout row keys, BMQ words
+  static constexpr int BUF = RK + BMQ * 4;
   static constexpr int NCH = D * S / 32;
   static constexpr int NOB = DP / 32;
   static constexpr int NQB = BMQ / 32;
@@ -177,13 +178,13 @@ struct DkvCfg {
   static constexpr int SMEM = 2 * BUF + (kVLds ? BNK * NROW : 0);
 };
 
-template <typename T, int D, int MASK>
+template <typename T, int D, int MASK, bool DROP>
 __global__ void __launch_bounds__(256)
     __attribute__((amdgpu_waves_per_eu(Elt<T>::kBytes == 2 ? 2 : 1, 8))) attn_bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     T* __restrict__ dK, T* __restrict__ dV, int n, int bh_count, int num_ktiles, int window,
-    float qk_scale, int qmode, float scale) {
+    float qk_scale, int qmode, float scale, DropParams dpar) {
   using C = DkvCfg<T, D>;
   constexpr int BMQ = C::BMQ;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -252,6 +253,7 @@ __global__ void __launch_bounds__(256)
   if constexpr (C::kDirect) tl.init(wave, lane);
   St sq, so;
   float4 lreg, dreg;  // LSE * log2(e) and delta for 4 rows (threads < BMQ / 4)
+  u32x4 kreg;         // dropout row keys of the same 4 rows (DROP)
 
   auto load_tile = [&](int t) {
     const int r0 = t * BMQ;
@@ -274,6 +276,7 @@ __global__ void __launch_bounds__(256)
         // rows past n contribute nothing: p = 2^(-inf) = 0
         lr[i] = r < n ? lv : INFINITY;
         dr[i] = r < n ? dv0 : 0.0f;
+        if constexpr (DROP) kreg[i] = drop_row_key(dpar, (uint32_t)bh, (uint32_t)r);
       }
     }
   };
@@ -288,6 +291,7 @@ __global__ void __launch_bounds__(256)
     if (tid < BMQ / 4) {
       *reinterpret_cast<float4*>(b + C::LS + 16 * tid) = lreg;
       *reinterpret_cast<float4*>(b + C::DL + 16 * tid) = dreg;
+      if constexpr (DROP) *reinterpret_cast<u32x4*>(b + C::RK + 16 * tid) = kreg;
     }
   };
 
@@ -352,12 +356,32 @@ __global__ void __launch_bounds__(256)
           const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dvl[4] = {d4.x, d4.y, d4.z, d4.w};
+          // Dropout (DROP): the four rows 32 qb + 8 g + 4 h + i against this
+          // lane's key.  Lane t of each group of four lanes (keys 4m .. 4m + 3)
+          // forms the keep bytes of row i = t for the four keys; a quad
+          // broadcast hands every lane byte (key & 3) of each row's word.
+          uint32_t kb[4] = {0u, 0u, 0u, 0u};
+          if constexpr (DROP) {
+            const int t = l32 & 3;
+            const uint32_t rk = reinterpret_cast<const uint32_t*>(b + C::RK)[32 * qb + 8 * g + 4 * h + t];
+            const uint32_t mine = drop_group_bytes(rk, (uint32_t)key >> 2);
+            kb[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
+            kb[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
+            kb[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
+            kb[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * g + i;
             const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lv[i]));
-            s[e] = p;
-            dp[e] = p * (dp[e] - dvl[i]);
+            if constexpr (DROP) {
+              const bool keep = drop_keep(kb[i], key & 3, dpar.thr);
+              s[e] = keep ? p : 0.0f;
+              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) - dvl[i]);
+            } else {
+              s[e] = p;
+              dp[e] = p * (dp[e] - dvl[i]);
+            }
           }
         }
         PChunks<T> pc, dsc;
@@ -386,6 +410,11 @@ __global__ void __launch_bounds__(256)
   }
 
   // Epilogue: lane holds column `key`, rows a = 32 ob + 8 g + 4 h + (0..3).
+  // With dropout, dV summed the kept weights unscaled: scale by 256 / (256 - thr).
+  if constexpr (DROP) {
+#pragma unroll
+    for (int ob = 0; ob < C::NOB; ++ob) dv[ob] *= dpar.inv_keep;
+  }
   if (key < n) {
     char* dkrow = reinterpret_cast<char*>(dK + (head + key) * D);
     char* dvrow = reinterpret_cast<char*>(dV + (head + key) * D);
@@ -440,12 +469,12 @@ struct DqCfg {
   static constexpr bool kDirect = kTr && D >= 32;
 };
 
-template <typename T, int D, int MASK>
+template <typename T, int D, int MASK, bool DROP>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     T* __restrict__ dQ, int n, int bh_count, int num_qtiles, int window, float qk_scale,
-    int qmode, float scale) {
+    int qmode, float scale, DropParams dpar) {
   using C = DqCfg<T, D>;
   constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
@@ -478,6 +507,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
   }
   const float lse2 = qrow < n ? LSE[head + qrow] * kLog2e : INFINITY;
   const float dlt = qrow < n ? delta[head + qrow] : 0.0f;
+  // Dropout (DROP): this row's key of the realized mask.
+  const uint32_t row_key = DROP ? drop_row_key(dpar, (uint32_t)bh, (uint32_t)qrow) : 0u;
 
   int kend = n;
   if (MASK != 0) kend = min(n, q0 + C::BM);
@@ -563,10 +594,25 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
             if (!key_allowed<MASK>(qrow, j, n, window)) s[e] = -INFINITY;
           }
         }
+        if constexpr (DROP) {
+          const int jb = j0 + 32 * sb + 4 * h;  // key of element e = 0
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
-          dp[e] = p * (dp[e] - dlt);
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t bytes = drop_group_bytes(row_key, (uint32_t)(jb + 8 * k) >> 2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int e = 4 * k + r;
+              const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
+              const bool keep = drop_keep(bytes, r, dpar.thr);
+              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) - dlt);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
+            dp[e] = p * (dp[e] - dlt);
+          }
         }
         PChunks<T> dsc;
         dsc.set(dp);
@@ -613,7 +659,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
-template <typename T, int D, int MASK>
+template <typename T, int D, int MASK, bool DROP>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   const int64_t rows = a.bh * a.n;
   if (a.stages & 1) {
@@ -628,36 +674,41 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   if (a.stages & 2) {
     using C = DkvCfg<T, D>;
     const int num_ktiles = (int)((a.n + C::BNK - 1) / C::BNK);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, MASK>), dim3((unsigned)(num_ktiles * a.bh)),
-                       dim3(C::kThreads), 0, a.stream, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dk),
-                       static_cast<T*>(a.dv), (int)a.n, (int)a.bh, num_ktiles, (int)a.window,
-                       a.qk_scale, a.qmode, a.scale);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, MASK, DROP>),
+                       dim3((unsigned)(num_ktiles * a.bh)), dim3(C::kThreads), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), (int)a.n, (int)a.bh,
+                       num_ktiles, (int)a.window, a.qk_scale, a.qmode, a.scale, a.drop);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.stages & 4) {
     using C = DqCfg<T, D>;
     const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK>), dim3((unsigned)(num_qtiles * a.bh)),
-                       dim3(C::kThreads), 0, a.stream, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dout), a.lse, a.delta, static_cast<T*>(a.dq),
-                       (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
-                       a.scale);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK, DROP>),
+                       dim3((unsigned)(num_qtiles * a.bh)), dim3(C::kThreads), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       static_cast<T*>(a.dq), (int)a.n, (int)a.bh, num_qtiles, (int)a.window,
+                       a.qk_scale, a.qmode, a.scale, a.drop);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+template <typename T, int D, int MASK>
+static hipError_t launch_bwd_m(const BwdArgs& a) {
+  return a.drop.thr > 0 ? launch_bwd_t<T, D, MASK, true>(a) : launch_bwd_t<T, D, MASK, false>(a);
+}
+
 template <typename T, int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   switch (a.mask) {
-    case 0: return launch_bwd_t<T, D, 0>(a);
-    case 1: return launch_bwd_t<T, D, 1>(a);
-    default: return launch_bwd_t<T, D, 2>(a);
+    case 0: return launch_bwd_m<T, D, 0>(a);
+    case 1: return launch_bwd_m<T, D, 1>(a);
+    default: return launch_bwd_m<T, D, 2>(a);
   }
 }
 

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_internal.h"
+
 namespace eiat {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -361,6 +363,44 @@ __device__ inline void store_transposed4(char* dst, int row_stride, const u32x4 
 }
 
 // Allowed-key membership for the three mask kinds (0 none, 1 causal, 2 window).
+// ---------------------------------------------------------------------------
+// Dropout mask (an extension; alphabetamath.cc, Algorithm "Exact tiled softmax
+// attention with block-recomputed vector-Jacobian products": the base method
+// has none, and an extension must replay the same realized mask in its
+// reverse pass).  The mask is a function of the indices, regenerated wherever
+// it is needed: for head bh (= b * H + h), row i and key j,
+//   row key  r_i  = XXH32 of the words (seed_hi, bh, i) with seed seed_lo,
+//   group    u    = XXH32 of the word (j >> 2) with seed r_i,
+//   keep_ij       = byte (j & 3) of u >= thr      (drop probability thr / 256),
+// and a kept weight is scaled by 256 / (256 - thr).  XXH32 is the 32-bit
+// xxHash function, here for messages of one and three 32-bit words.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t xxh32_round(uint32_t h, uint32_t w) {
+  h += w * 0xC2B2AE3Du;
+  return __builtin_rotateleft32(h, 17) * 0x27D4EB2Fu;
+}
+__device__ inline uint32_t xxh32_final(uint32_t h) {
+  h ^= h >> 15;
+  h *= 0x85EBCA77u;
+  h ^= h >> 13;
+  h *= 0xC2B2AE3Du;
+  return h ^ (h >> 16);
+}
+__device__ inline uint32_t drop_row_key(const DropParams& dp, uint32_t bh, uint32_t i) {
+  uint32_t h = dp.seed_lo + 0x165667B1u + 12u;
+  h = xxh32_round(h, dp.seed_hi);
+  h = xxh32_round(h, bh);
+  h = xxh32_round(h, i);
+  return xxh32_final(h);
+}
+// The four keep bytes of key group g (keys 4g .. 4g + 3) of a row.
+__device__ inline uint32_t drop_group_bytes(uint32_t row_key, uint32_t g) {
+  return xxh32_final(xxh32_round(row_key + 0x165667B1u + 4u, g));
+}
+__device__ inline bool drop_keep(uint32_t bytes, int r, int thr) {
+  return (int)((bytes >> (8 * r)) & 0xFFu) >= thr;
+}
+
 template <int MASK>
 __device__ inline bool key_allowed(int q, int j, int n, int window) {
   bool ok = j < n;

@@ -78,16 +78,13 @@ struct FwdCfg {
       S == 4 ? (D >= 128 ? 1 : 2) : ((D >= 128 || !__is_same(T, __bf16)) ? 2 : 3);
 };
 
-template <typename T, int D, int MASK>
+template <typename T, int D, int MASK, bool DROP>
 __global__ void
     __attribute__((amdgpu_flat_work_group_size(1, FwdCfg<T, D>::kThreads),
                    amdgpu_waves_per_eu(FwdCfg<T, D>::kMinWaves, 8)))
-    attn_fwd_kernel(const T* __restrict__ Q,
-                                                       const T* __restrict__ K,
-                                                       const T* __restrict__ V,
-                                                       T* __restrict__ O, float* __restrict__ LSE,
-                                                       int n, int bh_count, int num_qtiles,
-                                                       int window, float qk_scale, int qmode) {
+    attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                    T* __restrict__ O, float* __restrict__ LSE, int n, int bh_count,
+                    int num_qtiles, int window, float qk_scale, int qmode, DropParams dp) {
   using C = FwdCfg<T, D>;
   constexpr int BN = C::BN;
   // LDS: two K buffers, then two V buffers.  K runs one tile ahead of V.
@@ -108,6 +105,8 @@ __global__ void
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
+  // Dropout (DROP): this row's key of the realized mask (see attn_device.h).
+  const uint32_t row_key = DROP ? drop_row_key(dp, (uint32_t)bh, (uint32_t)qrow) : 0u;
 
   const int64_t head = (int64_t)bh * n;
   const char* Qh = reinterpret_cast<const char*>(Q + head * D);
@@ -240,7 +239,7 @@ __global__ void
   };
 
   // S^T block of tile t = K_t Q_w^T (fp32 accumulate)
-  auto qk = [&](int t, f32x16 (&s)[C::NSB]) {
+  auto qk = [&](int t, f32x16 (&s)[C::NSB]) __attribute__((always_inline)) {
     const char* kb = kbuf(t);
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
@@ -271,7 +270,7 @@ __global__ void
   // adds its sum to l and accumulates O^T += V^T P^T.  A tile with no allowed
   // key for some row leaves that row unchanged (its P is 0), as the
   // Algorithm's empty-block skip does.
-  auto prep_tile = [&](int t, f32x16 (&s)[C::NSB], auto masked) -> float {
+  auto prep_tile = [&](int t, f32x16 (&s)[C::NSB], auto masked) __attribute__((always_inline)) -> float {
     const int j0 = t * BN;
     if constexpr (decltype(masked)::value) {
 #pragma unroll
@@ -298,15 +297,33 @@ __global__ void
     // A row with no allowed key so far keeps the empty summary: shift by 0.
     return (m_run == -INFINITY) ? 0.0f : m_run;
   };
-  auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use) {
+  auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use) __attribute__((always_inline)) {
     const char* vb = vbuf(t);
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
       PChunks<T> pc;
-      pc.set(s[sb]);
-      l_run = chunk_sum<T>(pc, s[sb], l_run);
+      if constexpr (DROP) {
+        // l sums the undropped weights; then dropped weights become 0 in the
+        // value product (the kept ones are scaled by 256 / (256 - thr) at the end).
+        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ps[e & 3] += s[sb][e];
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        const int jb = t * BN + 32 * sb + 4 * h;  // key of element e = 0
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t bytes = drop_group_bytes(row_key, (uint32_t)(jb + 8 * k) >> 2);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!drop_keep(bytes, r, dp.thr)) s[sb][4 * k + r] = 0.0f;
+        }
+        pc.set(s[sb]);
+      } else {
+        pc.set(s[sb]);
+        l_run = chunk_sum<T>(pc, s[sb], l_run);
+      }
 #pragma unroll
       for (int ob = 0; ob < C::NOB; ++ob) {
 #pragma unroll
@@ -379,7 +396,7 @@ __global__ void
   // Epilogue: O = z / l in the input type, LSE = m + ln l (natural log).
   const float l_tot = halves_sum(l_run);
   if (qrow < n) {
-    const float inv = 1.0f / l_tot;
+    const float inv = (DROP ? dp.inv_keep : 1.0f) / l_tot;
     char* orow = reinterpret_cast<char*>(O + (head + qrow) * D);
 #pragma unroll
     for (int ob = 0; ob < C::NOB; ++ob)
@@ -402,24 +419,30 @@ __global__ void
   }
 }
 
-template <typename T, int D, int MASK>
+template <typename T, int D, int MASK, bool DROP>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdCfg<T, D>;
   const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
   const int64_t blocks = (int64_t)num_qtiles * a.bh;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, MASK>), dim3((unsigned)blocks), dim3(C::kThreads), 0,
-                     a.stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                     static_cast<const T*>(a.v), static_cast<T*>(a.o), a.lse, (int)a.n, (int)a.bh,
-                     num_qtiles, (int)a.window, a.qk_scale, a.qmode);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, MASK, DROP>), dim3((unsigned)blocks),
+                     dim3(C::kThreads), 0, a.stream, static_cast<const T*>(a.q),
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o),
+                     a.lse, (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
+                     a.drop);
   return hipGetLastError();
+}
+
+template <typename T, int D, int MASK>
+static hipError_t launch_fwd_m(const FwdArgs& a) {
+  return a.drop.thr > 0 ? launch_fwd_t<T, D, MASK, true>(a) : launch_fwd_t<T, D, MASK, false>(a);
 }
 
 template <typename T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
   switch (a.mask) {
-    case 0: return launch_fwd_t<T, D, 0>(a);
-    case 1: return launch_fwd_t<T, D, 1>(a);
-    default: return launch_fwd_t<T, D, 2>(a);
+    case 0: return launch_fwd_m<T, D, 0>(a);
+    case 1: return launch_fwd_m<T, D, 1>(a);
+    default: return launch_fwd_m<T, D, 2>(a);
   }
 }
 

@@ -7,6 +7,14 @@
 
 namespace eiat {
 
+// Dropout on the attention weights (mask definition with the device helpers
+// in attn_device.h).  thr == 0 means no dropout.
+struct DropParams {
+  uint32_t seed_lo, seed_hi;
+  int thr;          // 0..255: drop probability thr / 256
+  float inv_keep;   // 256 / (256 - thr)
+};
+
 // Arguments of one forward launch, already validated by the entry point.
 struct FwdArgs {
   const void* q;
@@ -22,6 +30,7 @@ struct FwdArgs {
   int64_t window;    // allowed keys per row (mask 2), clamped to n
   float qk_scale;    // |c| * log2(e), or 1 when c == 0
   int qmode;         // 0: c > 0, 1: c < 0 (Q negated), 2: c == 0 (Q taken as 0)
+  DropParams drop;   // drop.thr == 0: no dropout
   hipStream_t stream;
 };
 
@@ -46,6 +55,7 @@ struct BwdArgs {
   int qmode;
   float scale;       // c itself (multiplies dQ and dK)
   int stages;        // bit 0: delta, bit 1: dK/dV, bit 2: dQ
+  DropParams drop;   // the forward's dropout, replayed (thr == 0: none)
   hipStream_t stream;
 };
 

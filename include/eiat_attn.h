@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define EIAT_ABI_VERSION 2  /* 2: adds attn_decode */
+#define EIAT_ABI_VERSION 3  /* 2: adds attn_decode; 3: adds the dropout entry points */
 
 /* Symbols of the shared library (built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -136,6 +136,45 @@ EIAT_API eiat_status attn_bwd_stage(int stage, const void *q, const void *k, con
                                     void *stream);
 
 /* Static string naming a status code. */
+/*
+ * Forward and reverse with dropout on the attention weights.  The pages fix
+ * only the requirement (alphabetamath.cc, Algorithm "Exact tiled softmax
+ * attention with block-recomputed vector-Jacobian products", reverse
+ * procedure): the base method has no dropout, and an extension must replay
+ * the same realized mask in its reverse pass.  Here:
+ *
+ *     O_i = sum_j p_ij D_ij V_j,   D_ij = keep_ij * 256 / (256 - thr)
+ *
+ * with p_ij the undropped softmax weights (lse is the undropped log-normaliser)
+ * and thr = round(256 * p_drop) clamped to 255 (drop probability thr / 256).
+ * The realized mask is a function of (seed, b * H + h, i, j): row key
+ * r_i = XXH32(seed_hi | b*H+h | i; seed_lo) (three little-endian 32-bit words,
+ * XXH32 the 32-bit xxHash function), u = XXH32(j >> 2; r_i), keep_ij = byte
+ * (j & 3) of u >= thr.  The reverse calls regenerate it; pass the same p_drop
+ * and seed, and the o that the dropout forward wrote.  p_drop must be in
+ * [0, 1); p_drop = 0 gives exactly attn_fwd / attn_bwd.  Other arguments,
+ * layouts and errors as attn_fwd, attn_bwd and attn_bwd_stage.
+ */
+EIAT_API eiat_status attn_fwd_dropout(const void *q, const void *k, const void *v, void *o,
+                                      float *lse, int64_t B, int64_t H, int64_t n, int64_t d,
+                                      int64_t dv, int dtype, float scale, int mask,
+                                      int64_t window, float p_drop, uint64_t seed, void *stream);
+
+EIAT_API eiat_status attn_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
+                                      const void *dout, const float *lse, void *dq, void *dk,
+                                      void *dvv, void *workspace, size_t workspace_bytes,
+                                      int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                                      int dtype, float scale, int mask, int64_t window,
+                                      float p_drop, uint64_t seed, void *stream);
+
+EIAT_API eiat_status attn_bwd_dropout_stage(int stage, const void *q, const void *k,
+                                            const void *v, const void *o, const void *dout,
+                                            const float *lse, void *dq, void *dk, void *dvv,
+                                            void *workspace, size_t workspace_bytes, int64_t B,
+                                            int64_t H, int64_t n, int64_t d, int64_t dv,
+                                            int dtype, float scale, int mask, int64_t window,
+                                            float p_drop, uint64_t seed, void *stream);
+
 /*
  * Decode-shaped forward: a few new query rows per head against a long cache of
  * keys and values (the KV-cache setting of webturing.com.tr Principia,

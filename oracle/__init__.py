@@ -75,10 +75,10 @@ def _load():
         lib.oracle_decode.restype = ctypes.c_int
         u64 = ctypes.c_uint64
         lib.oracle_fwd_drop.argtypes = [i64, i64, i64, i64, ip, ip, ip, dbl, ctypes.c_int, i64,
-                                        u64, ctypes.c_int, ip, ip]
+                                        u64, ctypes.c_int, i64, ip, ip]
         lib.oracle_fwd_drop.restype = ctypes.c_int
         lib.oracle_bwd_drop.argtypes = [i64, i64, i64, i64, ip, ip, ip, ip, dbl, ctypes.c_int,
-                                        i64, u64, ctypes.c_int, ip, ip, ip, ip, ip, ip]
+                                        i64, u64, ctypes.c_int, i64, ip, ip, ip, ip, ip, ip]
         lib.oracle_bwd_drop.restype = ctypes.c_int
         lib.oracle_dropout_keep.argtypes = [u64, ctypes.c_int, i64, i64, i64,
                                             ctypes.POINTER(ctypes.c_int)]
@@ -168,9 +168,10 @@ def dropout_keep(seed: int, thr: int, bh: int, i: int, j: int) -> bool:
     return bool(out.value)
 
 
-def fwd_drop(q, k, v, scale: float, mask="none", window: int = 0, seed: int = 0, thr: int = 0):
+def fwd_drop(q, k, v, scale: float, mask="none", window: int = 0, seed: int = 0, thr: int = 0,
+             bh0: int = 0):
     """Dense forward with dropout on the weights; q, k, v [..., n, d]; the flat
-    leading index is the head index bh of the mask.  Returns (Y, LSE)."""
+    leading index plus bh0 is the head index bh of the mask.  Returns (Y, LSE)."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     lead = q.shape[:-2]
@@ -180,12 +181,13 @@ def fwd_drop(q, k, v, scale: float, mask="none", window: int = 0, seed: int = 0,
     y = np.empty((nh, n, dv))
     lse = np.empty((nh, n))
     _check(lib.oracle_fwd_drop(nh, n, d, dv, _ptr(q), _ptr(k), _ptr(v), float(scale),
-                               _mask_code(mask), int(window), seed, thr, _ptr(y), _ptr(lse)),
-           "fwd_drop")
+                               _mask_code(mask), int(window), seed, thr, int(bh0), _ptr(y),
+                               _ptr(lse)), "fwd_drop")
     return y.reshape(lead + (n, dv)), lse.reshape(lead + (n,))
 
 
-def bwd_drop(q, k, v, g, scale: float, mask="none", window: int = 0, seed: int = 0, thr: int = 0):
+def bwd_drop(q, k, v, g, scale: float, mask="none", window: int = 0, seed: int = 0, thr: int = 0,
+             bh0: int = 0):
     """VJP of sum(G * Y) for the forward with dropout (same mask replayed).
     Returns (dQ, dK, dV, Y, delta, LSE)."""
     lib = _load()
@@ -198,8 +200,8 @@ def bwd_drop(q, k, v, g, scale: float, mask="none", window: int = 0, seed: int =
     dvv, y = np.empty((nh, n, dv)), np.empty((nh, n, dv))
     delta, lse = np.empty((nh, n)), np.empty((nh, n))
     _check(lib.oracle_bwd_drop(nh, n, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
-                               _mask_code(mask), int(window), seed, thr, _ptr(dq), _ptr(dk),
-                               _ptr(dvv), _ptr(y), _ptr(delta), _ptr(lse)), "bwd_drop")
+                               _mask_code(mask), int(window), seed, thr, int(bh0), _ptr(dq),
+                               _ptr(dk), _ptr(dvv), _ptr(y), _ptr(delta), _ptr(lse)), "bwd_drop")
     sh = lead + (n,)
     return (dq.reshape(sh + (d,)), dk.reshape(sh + (d,)), dvv.reshape(sh + (dv,)),
             y.reshape(sh + (dv,)), delta.reshape(sh), lse.reshape(sh))

@@ -84,6 +84,7 @@ static double score(const double *qi, const double *kj, int64_t d, double c)
 typedef struct {
     uint64_t seed;
     int thr;
+    int64_t bh0; /* head index of the first head passed in */
 } drop_t;
 
 static uint32_t rotl32(uint32_t x, int r) { return (x << r) | (x >> (32 - r)); }
@@ -107,9 +108,9 @@ static uint32_t xxh32_words(const uint32_t *w, int nwords, uint32_t seed)
     return h;
 }
 
-static uint32_t drop_row_key(const drop_t *dr, int64_t bh, int64_t i)
+static uint32_t drop_row_key(const drop_t *dr, int64_t h, int64_t i)
 {
-    const uint32_t w[3] = {(uint32_t)(dr->seed >> 32), (uint32_t)bh, (uint32_t)i};
+    const uint32_t w[3] = {(uint32_t)(dr->seed >> 32), (uint32_t)(dr->bh0 + h), (uint32_t)i};
     return xxh32_words(w, 3, (uint32_t)dr->seed);
 }
 
@@ -134,7 +135,7 @@ int oracle_xxh32_words(const uint32_t *w, int nwords, uint32_t seed, uint32_t *o
 int oracle_dropout_keep(uint64_t seed, int thr, int64_t bh, int64_t i, int64_t j, int *keep)
 {
     if (thr < 0 || thr > 255 || bh < 0 || i < 0 || j < 0) return OR_EINVAL;
-    drop_t dr = {seed, thr};
+    drop_t dr = {seed, thr, 0};
     *keep = drop_factor(&dr, drop_row_key(&dr, bh, i), j) != 0.0;
     return OR_OK;
 }
@@ -235,13 +236,14 @@ int oracle_fwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
     return fwd_core(nh, n, d, dv, Q, K, V, c, mask, window, NULL, rows, nrows, Y, M, L, LSE);
 }
 
-/* The dense forward with the dropout above (head h of nh is bh = h). */
+/* The dense forward with the dropout above; head h of the nh passed in is
+ * head bh = bh0 + h of the mask. */
 int oracle_fwd_drop(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q,
                     const double *K, const double *V, double c, int mask, int64_t window,
-                    uint64_t seed, int thr, double *Y, double *LSE)
+                    uint64_t seed, int thr, int64_t bh0, double *Y, double *LSE)
 {
-    if (thr < 0 || thr > 255) return OR_EINVAL;
-    drop_t dr = {seed, thr};
+    if (thr < 0 || thr > 255 || bh0 < 0) return OR_EINVAL;
+    drop_t dr = {seed, thr, bh0};
     return fwd_core(nh, n, d, dv, Q, K, V, c, mask, window, &dr, NULL, n, Y, NULL, NULL, LSE);
 }
 
@@ -407,11 +409,11 @@ int oracle_bwd(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q, co
  */
 int oracle_bwd_drop(int64_t nh, int64_t n, int64_t d, int64_t dv, const double *Q,
                     const double *K, const double *V, const double *G, double c, int mask,
-                    int64_t window, uint64_t seed, int thr, double *dQ, double *dK, double *dV,
-                    double *Yout, double *Dout, double *LSEout)
+                    int64_t window, uint64_t seed, int thr, int64_t bh0, double *dQ, double *dK,
+                    double *dV, double *Yout, double *Dout, double *LSEout)
 {
-    if (thr < 0 || thr > 255) return OR_EINVAL;
-    drop_t dr = {seed, thr};
+    if (thr < 0 || thr > 255 || bh0 < 0) return OR_EINVAL;
+    drop_t dr = {seed, thr, bh0};
     return bwd_core(nh, n, d, dv, Q, K, V, G, c, mask, window, &dr, dQ, dK, dV, Yout, Dout,
                     LSEout);
 }

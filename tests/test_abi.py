@@ -17,12 +17,13 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = A.header_functions()
     assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
+                          "attn_fwd_dropout", "attn_bwd_dropout", "attn_bwd_dropout_stage",
                           "attn_decode", "attn_decode_stage", "attn_decode_workspace_bytes",
                           "attn_status_string",
                           "attn_last_error", "attn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -159,4 +160,22 @@ def test_decode_stage_rejects_unknown_stage(lib):
     assert lib.attn_decode_stage(2, *args) == 1
     assert lib.attn_decode_stage(-1, *args) == 1
     assert b"stage" in lib.attn_last_error()
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, 1.5, float("nan"), float("inf")])
+def test_dropout_rejects_probability(lib, p):
+    args = [F, F * 2**20, F * 2**21, F * 2**22, F * 2**23, 1, 1, 64, 64, 64, 2, 0.125, 1, 0]
+    assert lib.attn_fwd_dropout(*args, p, 7, None) == 1
+    assert b"p_drop" in lib.attn_last_error()
+    bargs = [F, F * 2**20, F * 2**21, F * 2**22, F * 2**23, F * 2**24, F * 2**25, F * 2**26,
+             F * 2**27, F * 2**28, 256, 1, 1, 64, 64, 64, 2, 0.125, 1, 0]
+    assert lib.attn_bwd_dropout(*bargs, p, 7, None) == 1
+    assert lib.attn_bwd_dropout_stage(1, *bargs, p, 7, None) == 1
+
+
+def test_dropout_checks_shapes_like_base(lib):
+    args = [F, F * 2**20, F * 2**21, F * 2**22, F * 2**23, 1, 1, 64, 32, 32, 2, 0.125, 1, 0]
+    assert lib.attn_fwd_dropout(*args, 0.1, 7, None) == 2  # d = 32 has no kernel
+    args = [F, F * 2**20, F * 2**21, F * 2**22, F * 2**23, 1, 1, 0, 64, 64, 2, 0.125, 1, 0]
+    assert lib.attn_fwd_dropout(*args, 0.1, 7, None) == 0  # empty: nothing to do
 

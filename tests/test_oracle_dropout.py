@@ -133,3 +133,15 @@ def test_mask_depends_on_every_key_part(oracle_mod):
         assert other != base, kw
     hi = [oracle_mod.dropout_keep(7 + (1 << 40), 128, 1, 2, j) for j in range(64)]
     assert hi != base  # the high seed word is part of the row key
+
+
+def test_head_offset_selects_the_head(oracle_mod):
+    """bh0 + h is the mask's head: the second of two heads equals that head alone at bh0 = 1."""
+    q, k, v, g = _inputs(6, 2, 12, 3, 3)
+    y2, l2 = oracle_mod.fwd_drop(q, k, v, 0.5, "causal", seed=9, thr=100)
+    y1, l1 = oracle_mod.fwd_drop(q[1:], k[1:], v[1:], 0.5, "causal", seed=9, thr=100, bh0=1)
+    np.testing.assert_array_equal(y2[1:], y1)
+    b2 = oracle_mod.bwd_drop(q, k, v, g, 0.5, "causal", seed=9, thr=100)
+    b1 = oracle_mod.bwd_drop(q[1:], k[1:], v[1:], g[1:], 0.5, "causal", seed=9, thr=100, bh0=1)
+    for a, b in zip(b2, b1):
+        np.testing.assert_array_equal(a[1:], b)
