@@ -253,6 +253,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="page_d64")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--p-drop", type=float, default=0.0,
+                    help="dropout probability on the weights (attn_fwd_dropout / attn_bwd_dropout)")
+    ap.add_argument("--seed", type=int, default=1, help="dropout mask seed")
     ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
                     help="override a workload field, e.g. --set n=16384 --set mask=none")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -304,17 +307,23 @@ def main():
     dcode, mcode = attn.DTYPE_CODES[dt], attn.MASK_CODES[w.mask]
     c = float(w.c)
 
+    pdrop, seed = float(args.p_drop), int(args.seed)
+
     def fwd():
-        s = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         B, H, n, d, dv, dcode, c, mcode, w.window, sh)
+        fa = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, n, d, dv,
+              dcode, c, mcode, w.window)
+        s = lib.attn_fwd_dropout(*fa, pdrop, seed, sh) if pdrop else lib.attn_fwd(*fa, sh)
         if s:
             raise attn.AttnError(s, lib.attn_last_error().decode())
 
     def bwd_stage(stage):
-        s = lib.attn_bwd_stage(stage, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                               do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                               dvv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, n, d, dv, dcode, c,
-                               mcode, w.window, sh)
+        ba = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dvv.data_ptr(), ws.data_ptr(),
+              ws_bytes, B, H, n, d, dv, dcode, c, mcode, w.window)
+        if pdrop:
+            s = lib.attn_bwd_dropout_stage(stage, *ba, pdrop, seed, sh)
+        else:
+            s = lib.attn_bwd_stage(stage, *ba, sh)
         if s:
             raise attn.AttnError(s, lib.attn_last_error().decode())
 
@@ -354,7 +363,7 @@ def main():
         achieved = amount / (kern_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = load_traffic(dom, w)
+    roof["traffic"] = None if pdrop else load_traffic(dom, w)  # counters were taken without dropout
 
     per_kernel = {}
     for name, ms in kern_ms.items():
@@ -392,7 +401,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
         "config": {"workload": f"{w.name}: B={B} H={H} n={n} d=v={d} {w.dtype} {w.mask}"
-                               + ("" if args.fwd_only else ", forward + backward"),
+                               + ("" if args.fwd_only else ", forward + backward")
+                               + (f", dropout p={pdrop}" if pdrop else ""),
                    "global_batch": B, "seq_len": n, "heads": H, "head_dim": d,
                    "mask": w.mask, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100.0 * value / peak, 2),
