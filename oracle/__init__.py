@@ -17,6 +17,11 @@ What each function follows (page title, then the named item on it):
 * ``fwd_tiled``  -- the Algorithm's forward procedure with key-block size b.
   ``broken=True`` plants the mistake of Night School "Fused attention",
   section "Forget one step" (no shrink of the running total).
+* ``mx_quant`` / ``mx_dequant`` / ``e4m3_*`` / ``fwht_f32`` -- webturing.com.tr
+  Principia, "Bellek Duvarinin Fizigi", section on FlashAttention-3: FP8
+  scores with block scaling and incoherent processing (random sign
+  multipliers); the block layout and code format are those of the OCP
+  microscaling FP8 (e4m3) format.
 
 Inputs are numpy arrays (any float dtype; converted to float64, which is exact
 for fp16/bf16/fp32 values), shaped ``[..., n, d]`` with leading dims flattened
@@ -86,6 +91,16 @@ def _load():
         lib.oracle_xxh32_words.argtypes = [ip, ctypes.c_int, ctypes.c_uint32,
                                            ctypes.POINTER(ctypes.c_uint32)]
         lib.oracle_xxh32_words.restype = ctypes.c_int
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = dbl
+        lib.oracle_e4m3_encode.argtypes = [dbl]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_fwht_f32.argtypes = [i64, ip]
+        lib.oracle_fwht_f32.restype = ctypes.c_int
+        lib.oracle_mx_quant.argtypes = [i64, i64, ip, ip, ip, ip]
+        lib.oracle_mx_quant.restype = ctypes.c_int
+        lib.oracle_mx_dequant.argtypes = [i64, i64, ip, ip, ip]
+        lib.oracle_mx_dequant.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -205,6 +220,56 @@ def bwd_drop(q, k, v, g, scale: float, mask="none", window: int = 0, seed: int =
     sh = lead + (n,)
     return (dq.reshape(sh + (d,)), dk.reshape(sh + (d,)), dvv.reshape(sh + (dv,)),
             y.reshape(sh + (dv,)), delta.reshape(sh), lse.reshape(sh))
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of one FP8 e4m3 code (NaN for 0x7F / 0xFF)."""
+    return _load().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(x: float) -> int:
+    """The e4m3 code nearest to x (|x| <= 448), ties to the even code."""
+    return int(_load().oracle_e4m3_encode(float(x)))
+
+
+def fwht_f32(x) -> np.ndarray:
+    """Unnormalized Walsh-Hadamard transform of one float32 vector, butterfly
+    stages of span 1, 2, ..., n/2, every sum rounded to float32."""
+    a = np.ascontiguousarray(x, dtype=np.float32).copy()
+    _check(_load().oracle_fwht_f32(a.size, _ptr(a)), "fwht_f32")
+    return a
+
+
+def mx_quant(x, signs=None):
+    """Block-scaled FP8 codes of rows x [..., d]: with ``signs`` (d values of
+    +-1) the rows are first rotated as H (signs * x) (incoherent processing);
+    then every 32 consecutive values share the scale 2^e, e the least with
+    max |x| <= 448 2^e.  Returns (codes uint8 [..., d], scale bytes e + 127
+    uint8 [..., ceil(d / 32)])."""
+    x = _f64(x)
+    d = x.shape[-1]
+    rows = x.size // d if d else 0
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.zeros(x.shape[:-1] + ((d + 31) // 32,), dtype=np.uint8)
+    sg = None if signs is None else np.ascontiguousarray(signs, dtype=np.int8)
+    if sg is not None and sg.shape != (d,):
+        raise ValueError("signs must have d entries")
+    _check(_load().oracle_mx_quant(rows, d, _ptr(x), None if sg is None else _ptr(sg),
+                                   _ptr(codes), _ptr(scales)), "mx_quant")
+    return codes, scales
+
+
+def mx_dequant(codes, scales) -> np.ndarray:
+    """Values of block-scaled codes (float64, exact)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    d = codes.shape[-1]
+    if scales.shape != codes.shape[:-1] + ((d + 31) // 32,):
+        raise ValueError("scales must be [..., ceil(d / 32)]")
+    out = np.zeros(codes.shape, dtype=np.float64)
+    _check(_load().oracle_mx_dequant(codes.size // d if d else 0, d, _ptr(codes), _ptr(scales),
+                                     _ptr(out)), "mx_dequant")
+    return out
 
 
 def bwd(q, k, v, g, scale: float, mask="none", window: int = 0):

@@ -528,6 +528,146 @@ int oracle_fwd_tiled(int64_t nh, int64_t n, int64_t d, int64_t dv, const double 
     return failed ? OR_ENOMEM : OR_OK;
 }
 
+/*
+ * Block-scaled FP8 inputs for the scores (an extension; webturing.com.tr
+ * Principia, "Bellek Duvarinin Fizigi", FlashAttention-3 section: FP8 with
+ * block-wise scaling and "incoherent processing", random sign multipliers,
+ * to hold the precision loss down).  Reading:
+ *   1. incoherent processing: x' = H (s * x), s a caller-given vector of
+ *      +-1 (the random draw is an input), H the unnormalized Sylvester
+ *      Walsh-Hadamard matrix of order d (H H^T = d I), so that for Q and K
+ *      rotated with the same s, Q' K'^T = d Q K^T;
+ *   2. block scaling (the OCP microscaling layout): each block of 32
+ *      consecutive values of a row gets a power-of-two scale 2^e, e the
+ *      smallest integer with max |x'| <= 448 * 2^e (448 the largest e4m3
+ *      value; at least -127, and 0 for an all-zero block), stored as the
+ *      byte e + 127, so no value saturates; the values are stored as the FP8
+ *      e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ *      infinities, largest 448) nearest to x' / 2^e, ties to even.
+ * The quantized codes are integers decided by floating point, so they are
+ * computed here in the precision the GPU kernel uses: float32, with the
+ * transform taken as butterfly stages of span 1, 2, 4, ..., d/2 (each pair
+ * (a, b) becomes (a + b, a - b), rounded to float32).
+ */
+
+/* Value of an FP8 e4m3 code (exact). */
+double oracle_e4m3_decode(uint8_t c)
+{
+    const int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
+    if (ex == 15 && man == 7) return NAN;
+    const double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(8.0 + man, ex - 10);
+    return sign ? -mag : mag;
+}
+
+/* The e4m3 code nearest to x (|x| <= 448, finite), ties to even code; the
+ * sign bit is x's own (so -0 and negatives that round to zero give 0x80). */
+uint8_t oracle_e4m3_encode(double x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    const double a = fabs(x);
+    /* candidate codes are monotone in value for 0..126: binary search the neighbours */
+    int lo = 0, hi = 126;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (oracle_e4m3_decode((uint8_t)mid) <= a) lo = mid; else hi = mid;
+    }
+    if (oracle_e4m3_decode((uint8_t)hi) <= a) lo = hi; /* a >= 448 */
+    int best = lo;
+    if (lo < 126) {
+        const double dl = a - oracle_e4m3_decode((uint8_t)lo);
+        const double dh = oracle_e4m3_decode((uint8_t)(lo + 1)) - a;
+        if (dh < dl || (dh == dl && ((lo + 1) & 1) == 0)) best = lo + 1;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* In-place unnormalized Walsh-Hadamard transform of n = 2^k floats, in the
+ * stage order stated above. */
+static void fwht_f32(float *x, int64_t n)
+{
+    for (int64_t span = 1; span < n; span <<= 1)
+        for (int64_t i = 0; i < n; i += 2 * span)
+            for (int64_t j = i; j < i + span; j++) {
+                const float a = x[j], b = x[j + span];
+                x[j] = a + b;
+                x[j + span] = a - b;
+            }
+}
+
+/* Exposed for the pins: the float32 transform of one vector. */
+int oracle_fwht_f32(int64_t n, float *x)
+{
+    if (n < 1 || (n & (n - 1))) return OR_EINVAL;
+    fwht_f32(x, n);
+    return OR_OK;
+}
+
+/* Smallest e >= -127 with amax <= 448 * 2^e (amax finite; 0 for amax = 0). */
+static int mx_exponent(float amax)
+{
+    if (amax == 0.0f) return 0;
+    int ex;
+    const double mant = frexp((double)amax, &ex); /* amax = mant 2^ex, mant in [0.5, 1) */
+    const int e = mant <= 0.875 ? ex - 9 : ex - 8;
+    return e < -127 ? -127 : e;
+}
+
+/*
+ * Quantize rows x [rows][d] with the incoherent processing and block scaling
+ * above.  signs [d] in {+1, -1} (NULL: no rotation, i.e. s = 1 and H = I; a
+ * rotation needs d a power of two).  Outputs codes [rows][d] and scale bytes
+ * [rows][ceil(d / 32)]; a last, shorter block takes its maximum over the
+ * values it has.
+ */
+int oracle_mx_quant(int64_t rows, int64_t d, const double *x, const int8_t *signs, uint8_t *codes,
+                    uint8_t *scales)
+{
+    if (rows < 0 || d < 1 || (signs && (d & (d - 1)))) return OR_EINVAL;
+    const int64_t nb = (d + 31) / 32;
+    int failed = 0;
+#pragma omp parallel
+    {
+        float *v = (float *)malloc(sizeof(float) * (size_t)d);
+        if (!v) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; r++) {
+            if (!v) continue;
+            for (int64_t k = 0; k < d; k++) {
+                v[k] = (float)x[r * d + k];
+                if (signs) v[k] = signs[k] < 0 ? -v[k] : v[k];
+            }
+            if (signs) fwht_f32(v, d);
+            for (int64_t b = 0; b < nb; b++) {
+                const int64_t k1 = b * 32 + 32 < d ? b * 32 + 32 : d;
+                float amax = 0.0f;
+                for (int64_t k = b * 32; k < k1; k++) amax = fmaxf(amax, fabsf(v[k]));
+                const int e = mx_exponent(amax);
+                scales[r * nb + b] = (uint8_t)(e + 127);
+                for (int64_t k = b * 32; k < k1; k++)
+                    codes[r * d + k] = oracle_e4m3_encode(ldexp((double)v[k], -e));
+            }
+        }
+        free(v);
+    }
+    return failed ? OR_ENOMEM : OR_OK;
+}
+
+/* Values of block-scaled codes: x[r][k] = value(code) * 2^(scale byte - 127). */
+int oracle_mx_dequant(int64_t rows, int64_t d, const uint8_t *codes, const uint8_t *scales,
+                      double *x)
+{
+    if (rows < 0 || d < 1) return OR_EINVAL;
+    const int64_t nb = (d + 31) / 32;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t k = 0; k < d; k++)
+            x[r * d + k] = ldexp(oracle_e4m3_decode(codes[r * d + k]),
+                                 (int)scales[r * nb + k / 32] - 127);
+    return OR_OK;
+}
+
 /* Number of OpenMP threads the oracle would use (reported by the benchmark). */
 int oracle_num_threads(void)
 {
