@@ -30,11 +30,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "fwd/bwd attention TFLOP/s, n=4096 d=64 bf16 causal; % of MFMA peak"
-# MI355X published dense peaks (TFLOP/s): bf16 / fp16 MFMA, fp32 MFMA
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+# MI355X published dense peaks (TFLOP/s): bf16 / fp16 MFMA, fp32 MFMA, fp8 MFMA
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8": 5033.2}
+# The FP8-score forward runs half its work (S = Q K^T) on the fp8 peak and half
+# (P V) on the 16-bit peak: its ceiling is the harmonic combination.
+PEAK_FP8_FWD = 1.0 / (0.5 / PEAK_TFLOPS["fp8"] + 0.5 / PEAK_TFLOPS["bf16"])
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip",
+                  "attn_fp8.hip"]
 DECODE_METRIC = ("decode attention GB/s: algorithmic HBM bytes (Q, K, V read once, O and LSE "
                  "written once) per second")
 
@@ -110,6 +114,132 @@ def cpu_baseline(w, budget_s: float):
                    f"same workload (n={w.n}, d={w.d}, {w.mask}); {t_total:.2f} s; "
                    f"full-workload time at this rate {t_total * total_heads / heads:.1f} s"),
     }
+
+
+def fp8_cpu_baseline(w, budget_s: float, signs):
+    """The oracle's FP8 path on whole heads: quantize Q and K (rotation and
+    block scales), dequantize, fp64 forward with c / d."""
+    import torch
+
+    import oracle
+    from exact_io_aware_tiled_amd.inputs import make_inputs
+
+    inp = make_inputs(w)
+    flat = {k_: t.reshape(-1, w.n, t.shape[-1]).to(torch.float64).numpy() for k_, t in inp.items()}
+    sg = signs.cpu().numpy()
+    per_head = 4.0 * w.d * convention_pairs(w.n, w.mask, w.window)
+    heads, t_total = 0, 0.0
+    for hh in range(flat["q"].shape[0]):
+        t0 = time.perf_counter()
+        qd = oracle.mx_dequant(*oracle.mx_quant(flat["q"][hh], sg))
+        kd = oracle.mx_dequant(*oracle.mx_quant(flat["k"][hh], sg))
+        oracle.fwd(qd[None], kd[None], flat["v"][hh][None], w.c / w.d, w.mask, w.window)
+        t_total += time.perf_counter() - t0
+        heads += 1
+        if t_total >= budget_s:
+            break
+    total_heads = flat["q"].shape[0]
+    return {
+        "value": per_head * heads / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"oracle FP8 quantizer + fp64 dense forward, {heads} of {total_heads} heads "
+                   f"of the same workload (n={w.n}, d={w.d}, {w.mask}); {t_total:.2f} s"),
+    }
+
+
+def bench_fp8(args, w):
+    """Forward with FP8 scores: a step quantizes Q and K from the 16-bit inputs
+    (rotation with one random sign vector, E8M0 block scales) and runs the FP8
+    forward; every kernel is timed on its own."""
+    import torch
+
+    from exact_io_aware_tiled_amd import attn
+    from exact_io_aware_tiled_amd.inputs import DTYPES, FP8_SIGNS_SEED, make_inputs, make_signs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = attn.load_library()
+    inp = make_inputs(w, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, H, n, d, dv = w.B, w.H, w.n, w.d, w.dv
+    dt = DTYPES[w.dtype]
+    signs = make_signs(d, FP8_SIGNS_SEED).to(dev)
+    q8 = torch.empty(B, H, n, d, dtype=torch.uint8, device=dev)
+    k8 = torch.empty_like(q8)
+    qs = torch.empty(B, H, n, d // 32, dtype=torch.uint8, device=dev)
+    ks = torch.empty_like(qs)
+    o = torch.empty(B, H, n, dv, dtype=dt, device=dev)
+    lse = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = attn._stream_handle(stream)
+    dcode, mcode = attn.DTYPE_CODES[dt], attn.MASK_CODES[w.mask]
+    rows = B * H * n
+
+    def chk(s):
+        if s:
+            raise attn.AttnError(s, lib.attn_last_error().decode())
+
+    def quant(x, codes, scales):
+        chk(lib.attn_quant_fp8(x.data_ptr(), signs.data_ptr(), codes.data_ptr(),
+                               scales.data_ptr(), rows, d, dcode, sh))
+
+    def fwd8():
+        chk(lib.attn_fwd_fp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
+                             v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, n, d, dv, dcode,
+                             float(w.c) / d, mcode, w.window, sh))
+
+    kernels = [("quant_q", lambda: quant(q, q8, qs)), ("quant_k", lambda: quant(k, k8, ks)),
+               ("attn_fwd_fp8", fwd8)]
+    log(f"bench: fp8 workload {w}")
+    K = args.steps
+    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream)
+    log("bench: kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in kern_ms.items()}))
+
+    bh = B * H
+    pairs = allowed_pairs(n, w.mask, w.window) * bh
+    conv_fwd = 4.0 * d * convention_pairs(n, w.mask, w.window) * bh
+    value = conv_fwd / (ms_per_step * 1e-3) / 1e12
+    e = 2 if dt != torch.float32 else 4
+    qbytes = float(rows * d * (e + 1) + rows * (d // 32) + d)  # read x, signs; write codes, scales
+    work = {"quant_q": ("hbm", qbytes), "quant_k": ("hbm", qbytes),
+            "attn_fwd_fp8": ("mfma", 4.0 * d * pairs)}
+    per_kernel = {}
+    for name, ms in kern_ms.items():
+        b_, amt = work[name]
+        rate = amt / (ms * 1e-3) / (1e12 if b_ == "mfma" else 1e9)
+        per_kernel[name] = {"ms": round(ms, 4), "bound": b_,
+                            ("tflops" if b_ == "mfma" else "gbs"): round(rate, 2)}
+    dom = "attn_fwd_fp8"
+    achieved = work[dom][1] / (kern_ms[dom] * 1e-3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": round(PEAK_FP8_FWD, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_FWD, 4), "traffic": load_traffic(dom, w)}
+    cpu = fp8_cpu_baseline(w, args.cpu_budget, signs) if args.cpu_budget > 0 else None
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"fp8-e4m3 scores (E8M0 block scales), {w.dtype} P and V",
+        "data": "synthetic (seeded N(0,1) Q, K, V; seeded random signs)",
+        "config": {"workload": (f"{w.name}: B={B} H={H} n={n} d=v={d} {w.dtype} {w.mask}, forward "
+                                "with FP8 scores: quantize Q and K + FP8 forward"),
+                   "global_batch": B, "seq_len": n, "heads": H, "head_dim": d,
+                   "mask": w.mask, "parallelism": "none (1 GPU)"},
+        "fwd_tflops": round(conv_fwd / (kern_ms[dom] * 1e-3) / 1e12, 2),
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def time_kernels(torch, kernels, warmup: int, steps: int, stream):
@@ -256,6 +386,8 @@ def main():
     ap.add_argument("--p-drop", type=float, default=0.0,
                     help="dropout probability on the weights (attn_fwd_dropout / attn_bwd_dropout)")
     ap.add_argument("--seed", type=int, default=1, help="dropout mask seed")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward with FP8 scores (attn_quant_fp8 on Q and K, then attn_fwd_fp8)")
     ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
                     help="override a workload field, e.g. --set n=16384 --set mask=none")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -289,6 +421,9 @@ def main():
         key, val = kv.split("=", 1)
         cur = getattr(w, key)
         w = w.replace(**{key: type(cur)(val) if cur is not None else float(val)})
+    if args.fp8:
+        bench_fp8(args, w)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = attn.load_library()

@@ -39,7 +39,7 @@ def header_functions() -> list[str]:
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"EIAT_API[^;(]*?\b(attn_[a-z_]+)\s*\(", text)
+    return re.findall(r"EIAT_API[^;(]*?\b(attn_[a-z0-9_]+)\s*\(", text)
 
 
 def load_library():
@@ -76,6 +76,12 @@ def load_library():
     lib.attn_decode_stage.restype = c_int
     lib.attn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    u8p = ctypes.c_void_p
+    lib.attn_quant_fp8.argtypes = [vp, vp, u8p, u8p, i64, i64, c_int, vp]
+    lib.attn_quant_fp8.restype = c_int
+    lib.attn_fwd_fp8.argtypes = [u8p, u8p, u8p, u8p, vp, vp, vp, i64, i64, i64, i64, i64, c_int,
+                                 c_float, c_int, i64, vp]
+    lib.attn_fwd_fp8.restype = c_int
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -131,6 +137,51 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, mask: str = "causal", windo
         _check(lib.attn_fwd_dropout(*args, float(p_drop), int(seed), _stream_handle(stream)))
     else:
         _check(lib.attn_fwd(*args, _stream_handle(stream)))
+    return out, lse
+
+
+def attn_quant_fp8(x, signs=None, codes=None, scales=None, stream=None):
+    """(codes, scales) of rows x [..., d] (attn_quant_fp8): uint8 e4m3 codes
+    [..., d] and E8M0 scale bytes [..., d / 32]; ``signs`` (int8 [d] of +-1 on
+    the GPU) rotates the rows as H (signs * x) first."""
+    lib = load_library()
+    _require(x, "x")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+    if signs is not None:
+        _require(signs, "signs")
+        if signs.dtype != torch.int8 or signs.numel() != d:
+            raise ValueError("signs must be int8 with d entries")
+    _check(lib.attn_quant_fp8(x.data_ptr(), None if signs is None else signs.data_ptr(),
+                              codes.data_ptr(), scales.data_ptr(), rows, d, DTYPE_CODES[x.dtype],
+                              _stream_handle(stream)))
+    return codes, scales
+
+
+def attn_fwd_fp8(q, q_scale, k, k_scale, v, scale: float, mask: str = "causal", window: int = 0,
+                 out=None, lse=None, stream=None):
+    """O, LSE with FP8 scores (attn_fwd_fp8).  q, k: uint8 e4m3 codes [B, H, n, d];
+    q_scale, k_scale: uint8 [B, H, n, d / 32]; v: [B, H, n, dv] f16/bf16.  ``scale``
+    multiplies the dequantized products (c / d for rows rotated by attn_quant_fp8)."""
+    lib = load_library()
+    for name, t in (("q", q), ("q_scale", q_scale), ("k", k), ("k_scale", k_scale), ("v", v)):
+        _require(t, name)
+    for name, t in (("q", q), ("q_scale", q_scale), ("k", k), ("k_scale", k_scale)):
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be uint8")
+    B, H, n, d, dv = _dims(q, v)
+    if out is None:
+        out = torch.empty(B, H, n, dv, dtype=v.dtype, device=v.device)
+    if lse is None:
+        lse = torch.empty(B, H, n, dtype=torch.float32, device=v.device)
+    _check(lib.attn_fwd_fp8(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
+                            v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n, d, dv,
+                            DTYPE_CODES[v.dtype], float(scale), MASK_CODES[mask], int(window),
+                            _stream_handle(stream)))
     return out, lse
 
 

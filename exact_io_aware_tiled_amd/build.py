@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libeiat_attn.so")
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fp8.hip"]
 # Machine-scheduler strategy per source, chosen by timing each kernel file's
 # kernels under the strategies LLVM offers for AMDGPU: the forward's
 # exp/MFMA interleave does best under max-ilp, the backward kernels (many

@@ -159,6 +159,95 @@ eiat_status attn_fwd_dropout(const void* q, const void* k, const void* v, void* 
   return fwd_impl(q, k, v, o, lse, B, H, n, d, dv, dtype, scale, mask, window, dp, stream);
 }
 
+eiat_status attn_quant_fp8(const void* x, const int8_t* signs, uint8_t* codes, uint8_t* scales,
+                           int64_t rows, int64_t d, int dtype, void* stream) {
+  if (rows < 0) return fail(EIAT_ERR_INVALID_ARG, "rows must be >= 0");
+  if (d < 1) return fail(EIAT_ERR_INVALID_ARG, "d must be >= 1");
+  if (dtype != EIAT_F32 && dtype != EIAT_F16 && dtype != EIAT_BF16)
+    return fail(EIAT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128)
+    return fail(EIAT_ERR_UNSUPPORTED, "FP8 quantization: d %lld has no kernel (64, 128)",
+                (long long)d);
+  // 256 threads cover 256 * 8 / d rows per workgroup
+  if ((rows + 15) / 16 > (int64_t)INT32_MAX) return fail(EIAT_ERR_UNSUPPORTED, "rows too large");
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (signs && !aligned16(signs)))
+    return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t xb = (size_t)(rows * d) * elem_bytes(dtype), cb = (size_t)(rows * d),
+               sb = (size_t)(rows * (d / 32));
+  if (overlaps(codes, cb, x, xb) || overlaps(scales, sb, x, xb) ||
+      (signs && (overlaps(codes, cb, signs, (size_t)d) || overlaps(scales, sb, signs, (size_t)d))))
+    return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap inputs");
+  if (overlaps(codes, cb, scales, sb)) return fail(EIAT_ERR_INVALID_ARG, "codes and scales overlap");
+  eiat::QuantArgs a;
+  a.x = x;
+  a.signs = signs;
+  a.codes = codes;
+  a.scales = scales;
+  a.rows = rows;
+  a.d = (int)d;
+  a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = eiat::launch_quant_fp8(a);
+  if (e != hipSuccess) return fail(EIAT_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+eiat_status attn_fwd_fp8(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k,
+                         const uint8_t* k_scale, const void* v, void* o, float* lse, int64_t B,
+                         int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale,
+                         int mask, int64_t window, void* stream) {
+  bool empty = false;
+  float qk_scale = 1.0f;
+  int qmode = 0;
+  int64_t win = 0;
+  eiat_status s =
+      check_common(B, H, n, d, dv, dtype, scale, mask, window, &empty, &qk_scale, &qmode, &win);
+  if (s != EIAT_OK) return s;
+  if (dtype == EIAT_F32)
+    return fail(EIAT_ERR_UNSUPPORTED, "FP8 scores: values and output are f16 or bf16");
+  if (d != 64 && d != 128)
+    return fail(EIAT_ERR_UNSUPPORTED, "FP8 scores: head dim %lld has no kernel (64, 128)",
+                (long long)d);
+  if (empty) return ok();
+  if (!q || !q_scale || !k || !k_scale || !v || !o || !lse)
+    return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
+  const void* ptrs[7] = {q, q_scale, k, k_scale, v, o, lse};
+  for (int i = 0; i < 7; ++i)
+    if (!aligned16(ptrs[i])) return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t qb = (size_t)(B * H * n * d), sb = (size_t)(B * H * n * (d / 32)),
+               vb = (size_t)(B * H * n * dv) * elem_bytes(dtype), lb = (size_t)(B * H * n) * 4;
+  const void* ins[5] = {q, q_scale, k, k_scale, v};
+  const size_t insz[5] = {qb, sb, qb, sb, vb};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(o, vb, ins[i], insz[i]) || overlaps(lse, lb, ins[i], insz[i]))
+      return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap inputs");
+  if (overlaps(o, vb, lse, lb)) return fail(EIAT_ERR_INVALID_ARG, "o and lse overlap");
+
+  eiat::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = n;
+  a.d = (int)d;
+  a.dtype = dtype;
+  a.mask = mask;
+  a.window = win;
+  a.qk_scale = qk_scale;
+  a.qmode = qmode;
+  a.drop = kNoDrop;
+  a.qscale = q_scale;
+  a.kscale = k_scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = eiat::launch_fwd(a);
+  if (e != hipSuccess) return fail(EIAT_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n) {
   if (B <= 0 || H <= 0 || n <= 0) return 0;
   return (size_t)B * (size_t)H * (size_t)n * sizeof(float);

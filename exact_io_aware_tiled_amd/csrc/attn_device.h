@@ -152,6 +152,46 @@ __device__ inline u32x4 keyrow_chunk(const char* row32, int ci, int h) {
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// FP8 (OCP e4m3) operands with E8M0 block scales: the gfx950 block-scaled
+// MFMA v_mfma_scale_f32_32x32x64_f8f6f4.  Lane L supplies 32 bytes of row
+// L % 32 of A (column L % 32 of B); the scale operand of lane r < 32 applies
+// to bytes 0-15 of lanes r and r + 32, that of lane r + 32 to bytes 16-31 of
+// both (checked on the GPU), so a lane's 32 bytes span two 32-value scale
+// blocks and each lane supplies the scale of one of them.  Byte OP of each
+// lane's scale word is the scale used (OP a constant operand select).
+// ---------------------------------------------------------------------------
+template <int OP>
+__device__ inline f32x16 mma_fp8(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u32x4 b_hi, uint32_t a_scale,
+                                 uint32_t b_scale, f32x16 c) {
+  const i32x8 a = {(int)a_lo[0], (int)a_lo[1], (int)a_lo[2], (int)a_lo[3],
+                   (int)a_hi[0], (int)a_hi[1], (int)a_hi[2], (int)a_hi[3]};
+  const i32x8 b = {(int)b_lo[0], (int)b_lo[1], (int)b_lo[2], (int)b_lo[3],
+                   (int)b_hi[0], (int)b_hi[1], (int)b_hi[2], (int)b_hi[3]};
+  // format 0 (fp8 e4m3) for both operands
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OP, (int)a_scale, OP,
+                                                         (int)b_scale);
+}
+
+// A row's E8M0 scale bytes (D / 32 of them at p) as the scale word of half-wave
+// h: byte 2c holds the scale of block 2c + h (chunk c of 64 values).
+template <int D>
+__device__ inline uint32_t scale_word(const uint8_t* p, int h) {
+  static_assert(D == 64 || D == 128, "FP8 scores: d is 64 or 128");
+  const uint32_t w = D == 64 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p)
+                             : *reinterpret_cast<const uint32_t*>(p);
+  return w >> (8 * h);
+}
+
+// Negate four e4m3 codes per word: flip the sign of every code with a nonzero
+// magnitude (zero stays the code 0x00).
+__device__ inline u32x4 fp8_negate(u32x4 w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] ^= ((w[i] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
+  return w;
+}
 
 // Copy rows [r0, r0 + R) of a [n][C * 16 bytes] global slice into an LDS tile
 // whose rows are C 16-byte chunks plus one padding chunk, with the gfx950

@@ -39,7 +39,7 @@
 
 namespace eiat {
 
-template <typename T, int D>
+template <typename T, int D, bool F8 = false>
 struct FwdCfg {
   // 16-bit d = 128 shares each K/V tile among 8 waves (256 query rows); the
   // others use 4 waves (128 rows), which balances the causal grid better.
@@ -50,16 +50,19 @@ struct FwdCfg {
   static constexpr int DP = D < 32 ? 32 : D;  // value rows padded to whole 32-row blocks
   static constexpr int S = Elt<T>::kBytes;
   static constexpr bool kTr = (S == 2);       // 16-bit: V row-major + transpose reads
-  static constexpr int KROW = D * S + 16;     // K tile row stride in LDS (bytes), padded
+  static constexpr int KS = F8 ? 1 : S;       // bytes per Q / K element (FP8 scores: 1)
+  static constexpr int KROW = D * KS + 16;    // K tile row stride in LDS (bytes), padded
   // V tile: row-major [BN][DP] (16-bit) or transposed [DP][BN] (float32)
   static constexpr int VROW = kTr ? DP * S + 16 : BN * S + 16;
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = (kTr ? BN : DP) * VROW;
   static constexpr int NCH = D * S / 32;      // d-chunks per 32x32 product (both halves)
+  static constexpr int NQF = F8 ? D / 32 : NCH;  // 16-byte Q chunks per lane
   static constexpr int NOB = DP / 32;         // 32-row blocks of O^T
   static constexpr int NSB = BN / 32;         // 32-key blocks of S^T
-  static constexpr int CPR = D * S / 16;      // 16-byte chunks per K / V row
-  static constexpr int KCHUNKS = BN * CPR;
+  static constexpr int CPR = D * S / 16;      // 16-byte chunks per V row
+  static constexpr int CPRK = D * KS / 16;    // 16-byte chunks per K row
+  static constexpr int KCHUNKS = BN * CPRK;
   static constexpr int KPT = (KCHUNKS + kThreads - 1) / kThreads;
   // V: 16-bit stages 16-byte chunks like K; float32 stages 4-key x 16-byte tasks
   static constexpr int VTASKS = kTr ? BN * CPR : (BN / 4) * CPR;
@@ -78,14 +81,15 @@ struct FwdCfg {
       S == 4 ? (D >= 128 ? 1 : 2) : ((D >= 128 || !__is_same(T, __bf16)) ? 2 : 3);
 };
 
-template <typename T, int D, int MASK, bool DROP>
+template <typename T, int D, int MASK, bool DROP, bool F8>
 __global__ void
-    __attribute__((amdgpu_flat_work_group_size(1, FwdCfg<T, D>::kThreads),
-                   amdgpu_waves_per_eu(FwdCfg<T, D>::kMinWaves, 8)))
-    attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    __attribute__((amdgpu_flat_work_group_size(1, FwdCfg<T, D, F8>::kThreads),
+                   amdgpu_waves_per_eu(FwdCfg<T, D, F8>::kMinWaves, 8)))
+    attn_fwd_kernel(const void* __restrict__ Q, const void* __restrict__ K, const T* __restrict__ V,
                     T* __restrict__ O, float* __restrict__ LSE, int n, int bh_count,
-                    int num_qtiles, int window, float qk_scale, int qmode, DropParams dp) {
-  using C = FwdCfg<T, D>;
+                    int num_qtiles, int window, float qk_scale, int qmode, DropParams dp,
+                    const uint8_t* __restrict__ Qsc, const uint8_t* __restrict__ Ksc) {
+  using C = FwdCfg<T, D, F8>;
   constexpr int BN = C::BN;
   // LDS: two K buffers, then two V buffers.  K runs one tile ahead of V.
   __shared__ __attribute__((aligned(16))) char smem[2 * C::KBYTES + 2 * C::VBYTES];
@@ -109,8 +113,8 @@ __global__ void
   const uint32_t row_key = DROP ? drop_row_key(dp, (uint32_t)bh, (uint32_t)qrow) : 0u;
 
   const int64_t head = (int64_t)bh * n;
-  const char* Qh = reinterpret_cast<const char*>(Q + head * D);
-  const char* Kh = reinterpret_cast<const char*>(K + head * D);
+  const char* Qh = reinterpret_cast<const char*>(Q) + head * D * C::KS;
+  const char* Kh = reinterpret_cast<const char*>(K) + head * D * C::KS;
   const char* Vh = reinterpret_cast<const char*>(V + head * D);
 
   // Key range any row of this workgroup may see; whole tiles outside it are skipped.
@@ -133,14 +137,37 @@ __global__ void
   // d-bytes [32c + 16h, 32c + 16h + 16).  The sign of c is folded into Q
   // (qmode 1), and c = 0 is taken as Q = 0 with a unit exponent scale (qmode 2).
   // Rows past n read row n - 1 (never stored).
-  u32x4 qf[C::NCH];
+  //
+  // FP8 scores (F8): Q and K are e4m3 codes with one E8M0 scale byte per 32
+  // values.  One block-scaled MFMA (K = 64) takes 32 bytes per lane: lane L
+  // supplies bytes [64 c + 16 h, +16) and [64 c + 32 + 16 h, +16) of its row
+  // for chunk c, and the scale of that row's 32-value block 2 c + h (the
+  // hardware applies the scale of lane r to bytes 0-15 of lanes r and r + 32,
+  // and that of lane r + 32 to bytes 16-31 of both).  Each lane's scale word
+  // holds its block 2 c + h in byte 2 c (operand select 2 c).
+  u32x4 qf[C::NQF];
+  uint32_t qsw = 0;
   {
     const int qr = min(qrow, n - 1);
+    if constexpr (F8) {
 #pragma unroll
-    for (int c = 0; c < C::NCH; ++c) {
-      qf[c] = ldg16(Qh + (int64_t)qr * D * C::S + 32 * c + 16 * h);
-      if (qmode == 1) qf[c] ^= Elt<T>::kSign;
-      if (qmode == 2) qf[c] = zero4();
+      for (int c = 0; c < D / 64; ++c) {
+        qf[2 * c] = ldg16(Qh + (int64_t)qr * D + 64 * c + 16 * h);
+        qf[2 * c + 1] = ldg16(Qh + (int64_t)qr * D + 64 * c + 32 + 16 * h);
+      }
+#pragma unroll
+      for (int c = 0; c < C::NQF; ++c) {
+        if (qmode == 1) qf[c] = fp8_negate(qf[c]);
+        if (qmode == 2) qf[c] = zero4();
+      }
+      qsw = scale_word<D>(Qsc + (head + qr) * (D / 32), h);
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c) {
+        qf[c] = ldg16(Qh + (int64_t)qr * D * C::S + 32 * c + 16 * h);
+        if (qmode == 1) qf[c] ^= Elt<T>::kSign;
+        if (qmode == 2) qf[c] = zero4();
+      }
     }
   }
 
@@ -163,7 +190,17 @@ __global__ void
   }
 
   TileLoader<BN, C::CPR, C::kWaves> tl;
-  if constexpr (C::kDirect) tl.init(wave, lane);
+  TileLoader<BN, C::CPRK, C::kWaves> tlk;
+  if constexpr (C::kDirect) {
+    tl.init(wave, lane);
+    if constexpr (F8) tlk.init(wave, lane);
+  }
+  // FP8: scale words of the K rows this lane supplies to the score MFMAs, for
+  // the tile being multiplied next (ksw) and the one being loaded (ksw_next).
+  uint32_t ksw[C::NSB], ksw_next[C::NSB];
+#pragma unroll
+  for (int sb = 0; sb < C::NSB; ++sb) ksw[sb] = ksw_next[sb] = 0;
+  const uint8_t* Ksh = F8 ? Ksc + head * (D / 32) : nullptr;
   u32x4 kreg[C::kDirect ? 1 : C::KPT];
   u32x4 vreg[C::kDirect ? 1 : C::VPT][C::VREGS];
 
@@ -171,7 +208,13 @@ __global__ void
   // zero probability (V), so the loads need no branch.
   auto load_k = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
-    if constexpr (C::kDirect) {
+    if constexpr (F8) {
+      tlk.load(kbuf(t), Kh, j0, n, wave, lane);
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb)
+        ksw_next[sb] = scale_word<D>(Ksh + (int64_t)min(j0 + 32 * sb + l32, n - 1) * (D / 32), h);
+      return;
+    } else if constexpr (C::kDirect) {
       tl.load(kbuf(t), Kh, j0, n, wave, lane);
       return;
     }
@@ -179,7 +222,7 @@ __global__ void
     for (int r = 0; r < C::KPT; ++r) {
       const int c = tid + r * C::kThreads;
       if (C::KCHUNKS % C::kThreads == 0 || c < C::KCHUNKS) {
-        const int key = c / C::CPR, col = c % C::CPR;
+        const int key = c / C::CPRK, col = c % C::CPRK;
         const int j = min(j0 + key, n - 1);
         kreg[r] = ldg16(Kh + (int64_t)j * D * C::S + col * 16);
       }
@@ -214,7 +257,7 @@ __global__ void
     for (int r = 0; r < C::KPT; ++r) {
       const int c = tid + r * C::kThreads;
       if (C::KCHUNKS % C::kThreads == 0 || c < C::KCHUNKS) {
-        const int key = c / C::CPR, col = c % C::CPR;
+        const int key = c / C::CPRK, col = c % C::CPRK;
         *reinterpret_cast<u32x4*>(kb + key * C::KROW + col * 16) = kreg[r];
       }
     }
@@ -245,10 +288,22 @@ __global__ void
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[sb][e] = 0.0f;
+      if constexpr (F8) {
+        const char* kr = kb + (32 * sb + l32) * C::KROW + 16 * h;
+        s[sb] = mma_fp8<0>(*reinterpret_cast<const u32x4*>(kr),
+                           *reinterpret_cast<const u32x4*>(kr + 32), qf[0], qf[1], ksw[sb], qsw,
+                           s[sb]);
+        if constexpr (D == 128)
+          s[sb] = mma_fp8<2>(*reinterpret_cast<const u32x4*>(kr + 64),
+                             *reinterpret_cast<const u32x4*>(kr + 96), qf[2], qf[3], ksw[sb], qsw,
+                             s[sb]);
+      } else {
 #pragma unroll
-      for (int c = 0; c < C::NCH; ++c) {
-        u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * sb + l32) * C::KROW + 32 * c + 16 * h);
-        s[sb] = Elt<T>::mma(a, qf[c], s[sb]);
+        for (int c = 0; c < C::NCH; ++c) {
+          u32x4 a =
+              *reinterpret_cast<const u32x4*>(kb + (32 * sb + l32) * C::KROW + 32 * c + 16 * h);
+          s[sb] = Elt<T>::mma(a, qf[c], s[sb]);
+        }
       }
     }
   };
@@ -341,16 +396,25 @@ __global__ void
 
   // Prologue: K_lo, V_lo and K_lo+1 in LDS, S_lo in registers.
   f32x16 sc[C::kDoubleS ? 2 : 1][C::NSB];
+  // FP8: the K scale words loaded with a tile become current for its product
+  auto advance_ksw = [&]() __attribute__((always_inline)) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) ksw[sb] = ksw_next[sb];
+    }
+  };
   load_k(t_lo);
   load_v(t_lo);
   store_k(t_lo);
   store_v(t_lo);
+  advance_ksw();
   if (t_lo + 1 < t_hi) {
     load_k(t_lo + 1);
     store_k(t_lo + 1);
   }
   __syncthreads();
   qk(t_lo, sc[0]);
+  advance_ksw();
   __syncthreads();  // K_lo is overwritten by K_lo+2 in the first iteration
 
   // Iteration t: the scores of tile t are exponentiated and multiplied into O
@@ -379,6 +443,7 @@ __global__ void
     __builtin_amdgcn_s_setprio(0);
     if (has1) store_v(t + 1);
     if (has2) store_k(t + 2);
+    advance_ksw();
     __syncthreads();
     if constexpr (C::kDoubleS) {
 #pragma unroll
@@ -419,22 +484,25 @@ __global__ void
   }
 }
 
-template <typename T, int D, int MASK, bool DROP>
+template <typename T, int D, int MASK, bool DROP, bool F8>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  using C = FwdCfg<T, D>;
+  using C = FwdCfg<T, D, F8>;
   const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
   const int64_t blocks = (int64_t)num_qtiles * a.bh;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, MASK, DROP>), dim3((unsigned)blocks),
-                     dim3(C::kThreads), 0, a.stream, static_cast<const T*>(a.q),
-                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o),
-                     a.lse, (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
-                     a.drop);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, MASK, DROP, F8>), dim3((unsigned)blocks),
+                     dim3(C::kThreads), 0, a.stream, a.q, a.k, static_cast<const T*>(a.v),
+                     static_cast<T*>(a.o), a.lse, (int)a.n, (int)a.bh, num_qtiles, (int)a.window,
+                     a.qk_scale, a.qmode, a.drop, a.qscale, a.kscale);
   return hipGetLastError();
 }
 
 template <typename T, int D, int MASK>
 static hipError_t launch_fwd_m(const FwdArgs& a) {
-  return a.drop.thr > 0 ? launch_fwd_t<T, D, MASK, true>(a) : launch_fwd_t<T, D, MASK, false>(a);
+  if constexpr (D >= 64 && Elt<T>::kBytes == 2) {
+    if (a.qscale) return launch_fwd_t<T, D, MASK, false, true>(a);
+  }
+  return a.drop.thr > 0 ? launch_fwd_t<T, D, MASK, true, false>(a)
+                        : launch_fwd_t<T, D, MASK, false, false>(a);
 }
 
 template <typename T, int D>

@@ -31,6 +31,10 @@ struct FwdArgs {
   float qk_scale;    // |c| * log2(e), or 1 when c == 0
   int qmode;         // 0: c > 0, 1: c < 0 (Q negated), 2: c == 0 (Q taken as 0)
   DropParams drop;   // drop.thr == 0: no dropout
+  // FP8 scores: q and k hold e4m3 codes with E8M0 scale bytes per 32 values
+  // ([bh][n][d / 32]); v, o stay in dtype (16-bit); d is 64 or 128.
+  const uint8_t* qscale = nullptr;
+  const uint8_t* kscale = nullptr;
   hipStream_t stream;
 };
 
@@ -79,10 +83,23 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+// Block-scaled FP8 quantization of rows (the FP8-score forward's Q and K).
+struct QuantArgs {
+  const void* x;          // [rows][d], dtype
+  const int8_t* signs;    // [d] of +-1, or null (no rotation)
+  uint8_t* codes;         // [rows][d] e4m3
+  uint8_t* scales;        // [rows][d / 32] E8M0 bytes
+  int64_t rows;
+  int d;                  // 64 or 128
+  int dtype;              // 0 f32, 1 f16, 2 bf16
+  hipStream_t stream;
+};
+
 // Cache ranges per (batch, key/value head) used by the decode kernels.
 int decode_splits(int64_t units, int64_t nk);
 
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_quant_fp8(const QuantArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 

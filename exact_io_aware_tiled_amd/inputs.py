@@ -157,3 +157,16 @@ def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None, device="cp
         out = {key: t.to(device) for key, t in out.items()}
     return out
 
+
+
+def make_signs(d: int, seed: int) -> torch.Tensor:
+    """The random sign vector of the FP8 path's incoherent processing: d values
+    of +-1 (int8), each sign drawn with probability 1/2 by a CPU generator."""
+    g = torch.Generator("cpu")
+    g.manual_seed(seed)
+    bits = torch.randint(0, 2, (d,), generator=g, dtype=torch.int64)
+    return (1 - 2 * bits).to(torch.int8)
+
+
+# Signs seed for the FP8 workloads (one vector per run, shared by Q and K).
+FP8_SIGNS_SEED = 3001

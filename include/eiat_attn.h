@@ -52,7 +52,8 @@
 extern "C" {
 #endif
 
-#define EIAT_ABI_VERSION 3  /* 2: adds attn_decode; 3: adds the dropout entry points */
+#define EIAT_ABI_VERSION 4  /* 2: adds attn_decode; 3: adds the dropout entry points;
+                               4: adds attn_quant_fp8 and attn_fwd_fp8 */
 
 /* Symbols of the shared library (built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -219,6 +220,50 @@ EIAT_API eiat_status attn_decode_stage(int stage, const void *q, const void *k, 
                                        size_t workspace_bytes, int64_t B, int64_t H, int64_t Hkv,
                                        int64_t nq, int64_t nk, int64_t d, int64_t dv, int dtype,
                                        float scale, int mask, int64_t window, void *stream);
+
+/*
+ * FP8 scores with block scaling and incoherent processing (webturing.com.tr
+ * Principia, "Bellek Duvarinin Fizigi", section on FlashAttention-3: FP8, with
+ * the precision loss held down by block scaling and random sign multipliers).
+ *
+ * attn_quant_fp8 turns rows x [rows][d] (dtype F32, F16 or BF16) into FP8
+ * codes with one scale per 32 values:
+ *   1. if signs is not NULL: x' = H (s * x), s_r = -1 where signs[r] < 0 and +1
+ *      otherwise, H the unnormalized Sylvester Walsh-Hadamard matrix of order d
+ *      (H H^T = d I), computed in float32 as butterfly stages of span 1, 2,
+ *      4, ..., d/2, each pair (a, b) becoming (a + b, a - b); else x' = x;
+ *   2. block b of a row (values 32 b .. 32 b + 31) gets e = the least integer
+ *      >= -127 with max |x'| <= 448 * 2^e (e = 0 for an all-zero block);
+ *      scales[row][b] = e + 127 (an E8M0 byte, the scale 2^e);
+ *   3. codes[row][r] = the OCP FP8 e4m3 code (1 sign, 4 exponent bits with
+ *      bias 7, 3 mantissa bits; largest 448) nearest to x'_r / 2^e, ties to
+ *      even.
+ * Rotate Q and K with the same signs: then Q' K'^T = d Q K^T, and the scale
+ * for attn_fwd_fp8 is c / d.  x must be finite.  Requires d in {64, 128}
+ * (other d >= 1: EIAT_ERR_UNSUPPORTED).  Device pointers, 16-byte aligned:
+ * x, codes [rows][d] bytes, scales [rows][d / 32] bytes, signs [d] int8 (or
+ * NULL); outputs must not overlap the inputs or each other.
+ */
+EIAT_API eiat_status attn_quant_fp8(const void *x, const int8_t *signs, uint8_t *codes,
+                                    uint8_t *scales, int64_t rows, int64_t d, int dtype,
+                                    void *stream);
+
+/*
+ * Forward with FP8 scores: the definition above with
+ *     s_ij = scale * sum_r Qd_ir Kd_jr,   Qd_ir = e4m3(q[i][r]) * 2^(q_scale[i][r / 32] - 127)
+ * (Kd likewise), i.e. attention of the dequantized rows, the score products
+ * taken on the block-scaled FP8 matrix cores with float32 accumulation.  The
+ * weights P and the value product stay in dtype (F16 or BF16) as in attn_fwd.
+ *   q, k      [B][H][n][d] e4m3 codes;  q_scale, k_scale  [B][H][n][d / 32] E8M0
+ *   v, o      [B][H][n][dv] dtype;      lse  [B][H][n] float32
+ * Masks, errors and the rest as attn_fwd; kernels for d == dv in {64, 128}
+ * and dtype F16 or BF16 (others: EIAT_ERR_UNSUPPORTED).  Codes 0x7F / 0xFF
+ * (NaN) must not occur (attn_quant_fp8 never writes them).
+ */
+EIAT_API eiat_status attn_fwd_fp8(const uint8_t *q, const uint8_t *q_scale, const uint8_t *k,
+                                  const uint8_t *k_scale, const void *v, void *o, float *lse,
+                                  int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
+                                  int dtype, float scale, int mask, int64_t window, void *stream);
 
 EIAT_API const char *attn_status_string(int status);
 

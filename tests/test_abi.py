@@ -19,11 +19,11 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
                           "attn_fwd_dropout", "attn_bwd_dropout", "attn_bwd_dropout_stage",
                           "attn_decode", "attn_decode_stage", "attn_decode_workspace_bytes",
-                          "attn_status_string",
+                          "attn_quant_fp8", "attn_fwd_fp8", "attn_status_string",
                           "attn_last_error", "attn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -179,3 +179,45 @@ def test_dropout_checks_shapes_like_base(lib):
     args = [F, F * 2**20, F * 2**21, F * 2**22, F * 2**23, 1, 1, 0, 64, 64, 2, 0.125, 1, 0]
     assert lib.attn_fwd_dropout(*args, 0.1, 7, None) == 0  # empty: nothing to do
 
+
+
+def quant(lib, x=F, signs=None, codes=F * 2**20, scales=F * 2**21, rows=100, d=64, dtype=2):
+    return lib.attn_quant_fp8(x, signs, codes, scales, rows, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), 1), (dict(codes=0), 1), (dict(scales=0), 1), (dict(rows=-1), 1), (dict(d=0), 1),
+    (dict(dtype=5), 1), (dict(x=F + 4), 1), (dict(signs=F * 2**22 + 8), 1),
+    (dict(codes=F), 1),  # codes overlap x
+    (dict(scales=F * 2**20 + 16), 1),  # scales overlap codes
+    (dict(d=32), 2), (dict(d=256), 2), (dict(d=48), 2),
+])
+def test_quant_fp8_rejects(lib, kw, code):
+    assert quant(lib, **kw) == code
+    assert lib.attn_last_error() != b""
+
+
+def test_quant_fp8_no_rows_is_ok_without_gpu(lib):
+    assert quant(lib, rows=0, x=0, codes=0, scales=0) == 0
+
+
+def fwd8(lib, q=F, qs=F * 2**20, k=F * 2**21, ks=F * 2**22, v=F * 2**23, o=F * 2**24,
+         lse=F * 2**25, B=1, H=1, n=64, d=64, dv=64, dtype=2, scale=0.125, mask=1, window=0):
+    return lib.attn_fwd_fp8(q, qs, k, ks, v, o, lse, B, H, n, d, dv, dtype, scale, mask, window,
+                            None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(qs=0), 1), (dict(ks=0), 1), (dict(B=-1), 1), (dict(mask=4), 1),
+    (dict(mask=2, window=0), 1), (dict(scale=float("nan")), 1), (dict(qs=F * 2**20 + 1), 1),
+    (dict(o=F * 2**21), 1),  # output overlaps k
+    (dict(dtype=0), 2),  # float32 values: no FP8 kernel
+    (dict(d=16, dv=16), 2), (dict(d=64, dv=128), 2), (dict(d=32, dv=32), 2),
+])
+def test_fwd_fp8_rejects(lib, kw, code):
+    assert fwd8(lib, **kw) == code
+    assert lib.attn_last_error() != b""
+
+
+def test_fwd_fp8_empty_is_ok_without_gpu(lib):
+    assert fwd8(lib, n=0, q=0, qs=0, k=0, ks=0, v=0, o=0, lse=0) == 0
