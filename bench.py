@@ -216,6 +216,8 @@ def bench_fp8(args, w):
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
             "peak": round(PEAK_FP8_FWD, 1), "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP8_FWD, 4), "traffic": load_traffic(dom, w)}
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.copy_calibration)
     cpu = fp8_cpu_baseline(w, args.cpu_budget, signs) if args.cpu_budget > 0 else None
     line = {
         "metric": METRIC,
@@ -240,6 +242,17 @@ def bench_fp8(args, w):
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_calibration(torch, dev, mib: int):
+    """One plain device copy of `mib` MiB, the reference the HBM counters are scaled by."""
+    nbytes = mib << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: copy calibration {nbytes} bytes read, {nbytes} bytes written")
 
 
 def time_kernels(torch, kernels, warmup: int, steps: int, stream):
@@ -342,13 +355,7 @@ def bench_decode(args, w):
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": load_traffic(dom, w)}
     if args.copy_calibration:
-        nbytes = args.copy_calibration << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"bench: copy calibration {nbytes} bytes read, {nbytes} bytes written")
+        copy_calibration(torch, dev, args.copy_calibration)
     cpu = decode_cpu_baseline(w, args.cpu_budget) if args.cpu_budget > 0 else None
     line = {
         "metric": DECODE_METRIC,
@@ -508,13 +515,7 @@ def main():
                             ("tflops" if b_ == "mfma" else "gbs"): round(rate, 2)}
 
     if args.copy_calibration:
-        nbytes = args.copy_calibration << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"bench: copy calibration {nbytes} bytes read, {nbytes} bytes written")
+        copy_calibration(torch, dev, args.copy_calibration)
 
     cpu = None
     if args.cpu_budget > 0:
