@@ -72,9 +72,9 @@ def sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload) -> float | None:
-    """Counter-derived HBM bytes per launch, if taken on the current kernel
-    sources and on this exact workload (else None)."""
+def _counter_entry(kernel: str, workload) -> dict | None:
+    """The committed rocprofv3 counter summary of `kernel` on this exact
+    workload, if it was taken on the current kernel sources (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
@@ -82,8 +82,21 @@ def load_traffic(kernel: str, workload) -> float | None:
         return None
     if data.get("sources_sha") != sources_digest():
         return None
-    entry = data.get("workloads", {}).get(repr(workload), {}).get("kernels", {}).get(kernel)
+    return data.get("workloads", {}).get(repr(workload), {}).get("kernels", {}).get(kernel)
+
+
+def load_traffic(kernel: str, workload) -> float | None:
+    """Counter-derived HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated)."""
+    entry = _counter_entry(kernel, workload)
     return entry.get("bytes_per_launch") if entry else None
+
+
+def load_activity(kernel: str, workload) -> dict | None:
+    """MFMA busy share, LDS bank-conflict stall share and VALU/MFMA instruction
+    ratio of `kernel` from the committed rocprofv3 pass."""
+    entry = _counter_entry(kernel, workload)
+    act = entry.get("activity") if entry else None
+    return {"kernel": kernel, **act, "source": "profiles/attn_activity_counters.txt"} if act else None
 
 
 def cpu_baseline(w, budget_s: float):
@@ -239,6 +252,7 @@ def bench_fp8(args, w):
         "fwd_tflops": round(conv_fwd / (kern_ms[dom] * 1e-3) / 1e12, 2),
         "kernels": per_kernel,
         "roofline": roof,
+        "counters": load_activity(dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -378,6 +392,7 @@ def bench_decode(args, w):
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "kernels": per_kernel,
         "roofline": roof,
+        "counters": load_activity(dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -546,6 +561,7 @@ def main():
         "bwd_tflops": None if args.fwd_only else round(conv_bwd / (bwd_ms * 1e-3) / 1e12, 2),
         "kernels": per_kernel,
         "roofline": roof,
+        "counters": None if pdrop else load_activity(dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
