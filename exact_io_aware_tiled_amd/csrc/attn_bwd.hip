@@ -167,7 +167,7 @@ struct DkvCfg {
   static constexpr int ON = QT + TBYTES;
   static constexpr int OT = ON + BMQ * NROW;
   static constexpr int LS = OT + TBYTES;             // LSE * log2(e), BMQ floats
-  static constexpr int DL = LS + BMQ * 4;            // delta, BMQ floats
+  static constexpr int DL = LS + BMQ * 4;            // -delta, BMQ floats
   static constexpr int RK = DL + BMQ * 4;            // dropout row keys, BMQ words
   static constexpr int BUF = RK + BMQ * 4;
   static constexpr int NCH = D * S / 32;
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(256)
         const float lv = LSEh[rc] * kLog2e, dv0 = Dh[rc];
         // rows past n contribute nothing: p = 2^(-inf) = 0
         lr[i] = r < n ? lv : INFINITY;
-        dr[i] = r < n ? dv0 : 0.0f;
+        dr[i] = r < n ? -dv0 : 0.0f;  // -delta: the dP accumulator starts from it
         if constexpr (DROP) kreg[i] = drop_row_key(dpar, (uint32_t)bh, (uint32_t)r);
       }
     }
@@ -323,12 +323,26 @@ __global__ void __launch_bounds__(256)
 
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
-        // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys
+        // S = Q K^T and dP - delta = dO V^T - delta for 32 query rows x this
+        // wave's 32 keys (without dropout the dP accumulator starts at -delta of
+        // its row, so dS = p (dP - delta) needs no subtraction afterwards)
+        const float* ls = reinterpret_cast<const float*>(b + C::LS);
+        const float* dl = reinterpret_cast<const float*>(b + C::DL);  // -delta
         f32x16 s, dp;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s[e] = 0.0f;
-          dp[e] = 0.0f;
+        for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+        if constexpr (DROP) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) dp[e] = 0.0f;
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
+            dp[4 * g] = d4.x;
+            dp[4 * g + 1] = d4.y;
+            dp[4 * g + 2] = d4.z;
+            dp[4 * g + 3] = d4.w;
+          }
         }
         const int rq = 32 * qb + l32;
 #pragma unroll
@@ -352,14 +366,18 @@ __global__ void __launch_bounds__(256)
           }
         }
         // p = 2^(s c log2 e - LSE log2 e), dS = p (dP - delta)
-        const float* ls = reinterpret_cast<const float*>(b + C::LS);
-        const float* dl = reinterpret_cast<const float*>(b + C::DL);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const float4 l4 = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * g + 4 * h);
-          const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dvl[4] = {d4.x, d4.y, d4.z, d4.w};
+          float ndl[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // -delta (dropout path only)
+          if constexpr (DROP) {
+            const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
+            ndl[0] = d4.x;
+            ndl[1] = d4.y;
+            ndl[2] = d4.z;
+            ndl[3] = d4.w;
+          }
           // Dropout (DROP): the four rows 32 qb + 8 g + 4 h + i against this
           // lane's key.  Lane t of each group of four lanes (keys 4m .. 4m + 3)
           // forms the keep bytes of row i = t for the four keys; a quad
@@ -381,10 +399,10 @@ __global__ void __launch_bounds__(256)
             if constexpr (DROP) {
               const bool keep = drop_keep(kb[i], key & 3, dpar.thr);
               s[e] = keep ? p : 0.0f;
-              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) - dvl[i]);
+              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) + ndl[i]);
             } else {
               s[e] = p;
-              dp[e] = p * (dp[e] - dvl[i]);
+              dp[e] = p * dp[e];
             }
           }
         }
@@ -577,11 +595,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) {
         // S^T = K Q^T and dP^T = V dO^T: lane holds one query row, 16 keys per half
+        // (without dropout dP^T starts at -delta of the lane's row, so
+        // dS = p (dP - delta) needs no subtraction afterwards)
         f32x16 s, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           s[e] = 0.0f;
-          dp[e] = 0.0f;
+          dp[e] = DROP ? 0.0f : -dlt;
         }
         const int rk = 32 * sb + l32;
 #pragma unroll
@@ -615,7 +635,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
-            dp[e] = p * (dp[e] - dlt);
+            dp[e] = p * dp[e];
           }
         }
         PChunks<T> dsc;
