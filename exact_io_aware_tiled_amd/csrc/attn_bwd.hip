@@ -22,6 +22,8 @@
 // The transposed operands (dO^T, Q^T, K^T) are read from the natural LDS tiles
 // with ds_read_b64_tr_b16 for 16-bit types; float32 writes transposed copies
 // while staging, from the same registers that hold the natural copies.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -144,6 +146,12 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const T* __restrict
 // ---------------------------------------------------------------------------
 // 2. dK / dV: keys resident, query tiles streamed
 // ---------------------------------------------------------------------------
+// Whether a tile body applies the per-element mask: a compile-time flag
+// (std::true_type / std::false_type) or a run-time one (bool).
+__device__ inline bool mask_on(bool m) { return m; }
+template <bool B>
+__device__ constexpr bool mask_on(std::integral_constant<bool, B>) { return B; }
+
 template <typename T, int D>
 struct DkvCfg {
   static constexpr int kWaves = 4;
@@ -305,7 +313,17 @@ __global__ void __launch_bounds__(256)
   }
   __syncthreads();
 
-  for (int t = t_lo; t < t_hi; ++t) {
+  // Query tiles [ta, tb) need no per-element mask for any key of this wave
+  // (every row sees every key); the others straddle a mask boundary or hold
+  // keys past n.  The three ranges run as separate loops, so the interior
+  // body has no mask and no branch.
+  int ta = t_lo, tb = t_hi;
+  if (MASK != 0) ta = min(t_hi, max(t_lo, (kw0 + 31 + BMQ - 1) / BMQ));
+  if (MASK == 2) tb = min(t_hi, (kw0 + window) / BMQ);
+  if (kw0 + 32 > n) ta = t_hi;
+  tb = max(tb, ta);
+
+  auto iterate = [&](int t, auto masked) __attribute__((always_inline)) {
     const int buf = (t - t_lo) & 1;
     const bool has_next = t + 1 < t_hi;
     if (has_next) load_tile(t + 1);
@@ -316,119 +334,130 @@ __global__ void __launch_bounds__(256)
     if (MASK == 2) empty = empty || (qt0 > kw0 + 31 + window - 1);
     if (!empty) {
       const char* b = smem + buf * C::BUF;
-      bool straddle = false;
-      if (MASK != 0) straddle = qt0 < kw0 + 31;
-      if (MASK == 2) straddle = straddle || (qt0 + BMQ - 1 - window + 1 > kw0);
-      straddle = straddle || (kw0 + 32 > n);
 
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
-        // S = Q K^T and dP - delta = dO V^T - delta for 32 query rows x this
-        // wave's 32 keys (without dropout the dP accumulator starts at -delta of
-        // its row, so dS = p (dP - delta) needs no subtraction afterwards)
-        const float* ls = reinterpret_cast<const float*>(b + C::LS);
-        const float* dl = reinterpret_cast<const float*>(b + C::DL);  // -delta
-        f32x16 s, dp;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.0f;
-        if constexpr (DROP) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) dp[e] = 0.0f;
-        } else {
-#pragma unroll
+      // One tile, with the per-element mask compiled in or out, so that the
+      // unmasked body has no branch and the scheduler can overlap the 32-row
+      // blocks (the next block's LDS reads and MFMAs with this one's exponentials).
+      auto tile_body = [&](auto masked) __attribute__((always_inline)) {
+  #pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          // S = Q K^T and dP - delta = dO V^T - delta for 32 query rows x this
+          // wave's 32 keys (without dropout the dP accumulator starts at -delta of
+          // its row, so dS = p (dP - delta) needs no subtraction afterwards)
+          const float* ls = reinterpret_cast<const float*>(b + C::LS);
+          const float* dl = reinterpret_cast<const float*>(b + C::DL);  // -delta
+          f32x16 s, dp;
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+          if constexpr (DROP) {
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) dp[e] = 0.0f;
+          } else {
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
+              dp[4 * g] = d4.x;
+              dp[4 * g + 1] = d4.y;
+              dp[4 * g + 2] = d4.z;
+              dp[4 * g + 3] = d4.w;
+            }
+          }
+          const int rq = 32 * qb + l32;
+  #pragma unroll
+          for (int c = 0; c < C::NCH; ++c) {
+            u32x4 qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
+            u32x4 oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
+            s = Elt<T>::mma(qa, kf[c], s);
+            u32x4 vb4;
+            if constexpr (C::kVLds)
+              vb4 = *reinterpret_cast<const u32x4*>(smem + C::VRES + (32 * wave + l32) * C::NROW +
+                                                    32 * c + 16 * h);
+            else
+              vb4 = vf[c];
+            dp = Elt<T>::mma(oa, vb4, dp);
+          }
+          if (mask_on(masked)) {
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int q = qt0 + 32 * qb + 8 * (e >> 2) + 4 * h + (e & 3);
+              if (!key_allowed<MASK>(q, key, n, window)) s[e] = -INFINITY;
+            }
+          }
+          // p = 2^(s c log2 e - LSE log2 e), dS = p (dP - delta)
+  #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
-            dp[4 * g] = d4.x;
-            dp[4 * g + 1] = d4.y;
-            dp[4 * g + 2] = d4.z;
-            dp[4 * g + 3] = d4.w;
-          }
-        }
-        const int rq = 32 * qb + l32;
-#pragma unroll
-        for (int c = 0; c < C::NCH; ++c) {
-          u32x4 qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
-          u32x4 oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
-          s = Elt<T>::mma(qa, kf[c], s);
-          u32x4 vb4;
-          if constexpr (C::kVLds)
-            vb4 = *reinterpret_cast<const u32x4*>(smem + C::VRES + (32 * wave + l32) * C::NROW +
-                                                  32 * c + 16 * h);
-          else
-            vb4 = vf[c];
-          dp = Elt<T>::mma(oa, vb4, dp);
-        }
-        if (straddle) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int q = qt0 + 32 * qb + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (!key_allowed<MASK>(q, key, n, window)) s[e] = -INFINITY;
-          }
-        }
-        // p = 2^(s c log2 e - LSE log2 e), dS = p (dP - delta)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 l4 = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * g + 4 * h);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          float ndl[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // -delta (dropout path only)
-          if constexpr (DROP) {
-            const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
-            ndl[0] = d4.x;
-            ndl[1] = d4.y;
-            ndl[2] = d4.z;
-            ndl[3] = d4.w;
-          }
-          // Dropout (DROP): the four rows 32 qb + 8 g + 4 h + i against this
-          // lane's key.  Lane t of each group of four lanes (keys 4m .. 4m + 3)
-          // forms the keep bytes of row i = t for the four keys; a quad
-          // broadcast hands every lane byte (key & 3) of each row's word.
-          uint32_t kb[4] = {0u, 0u, 0u, 0u};
-          if constexpr (DROP) {
-            const int t = l32 & 3;
-            const uint32_t rk = reinterpret_cast<const uint32_t*>(b + C::RK)[32 * qb + 8 * g + 4 * h + t];
-            const uint32_t mine = drop_group_bytes(rk, (uint32_t)key >> 2);
-            kb[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
-            kb[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
-            kb[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
-            kb[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * g + i;
-            const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lv[i]));
+            const float4 l4 = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * g + 4 * h);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            float ndl[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // -delta (dropout path only)
             if constexpr (DROP) {
-              const bool keep = drop_keep(kb[i], key & 3, dpar.thr);
-              s[e] = keep ? p : 0.0f;
-              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) + ndl[i]);
-            } else {
-              s[e] = p;
-              dp[e] = p * dp[e];
+              const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
+              ndl[0] = d4.x;
+              ndl[1] = d4.y;
+              ndl[2] = d4.z;
+              ndl[3] = d4.w;
+            }
+            // Dropout (DROP): the four rows 32 qb + 8 g + 4 h + i against this
+            // lane's key.  Lane t of each group of four lanes (keys 4m .. 4m + 3)
+            // forms the keep bytes of row i = t for the four keys; a quad
+            // broadcast hands every lane byte (key & 3) of each row's word.
+            uint32_t kb[4] = {0u, 0u, 0u, 0u};
+            if constexpr (DROP) {
+              const int t = l32 & 3;
+              const uint32_t rk = reinterpret_cast<const uint32_t*>(b + C::RK)[32 * qb + 8 * g + 4 * h + t];
+              const uint32_t mine = drop_group_bytes(rk, (uint32_t)key >> 2);
+              kb[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
+              kb[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
+              kb[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
+              kb[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
+            }
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int e = 4 * g + i;
+              const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lv[i]));
+              if constexpr (DROP) {
+                const bool keep = drop_keep(kb[i], key & 3, dpar.thr);
+                s[e] = keep ? p : 0.0f;
+                dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) + ndl[i]);
+              } else {
+                s[e] = p;
+                dp[e] = p * dp[e];
+              }
+            }
+          }
+          PChunks<T> pc, dsc;
+          pc.set(s);
+          dsc.set(dp);
+  #pragma unroll
+          for (int ob = 0; ob < C::NOB; ++ob) {
+  #pragma unroll
+            for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+              u32x4 oa, qa2;
+              if constexpr (C::kTr) {
+                oa = tr_chunk(b + C::ON, C::NROW, 32 * qb, ob, ci, lane);
+                qa2 = tr_chunk(b + C::QN, C::NROW, 32 * qb, ob, ci, lane);
+              } else {
+                oa = keyrow_chunk<T>(b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
+                qa2 = keyrow_chunk<T>(b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
+              }
+              dv[ob] = Elt<T>::mma(oa, pc.c[ci], dv[ob]);
+              dk[ob] = Elt<T>::mma(qa2, dsc.c[ci], dk[ob]);
             }
           }
         }
-        PChunks<T> pc, dsc;
-        pc.set(s);
-        dsc.set(dp);
-#pragma unroll
-        for (int ob = 0; ob < C::NOB; ++ob) {
-#pragma unroll
-          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
-            u32x4 oa, qa2;
-            if constexpr (C::kTr) {
-              oa = tr_chunk(b + C::ON, C::NROW, 32 * qb, ob, ci, lane);
-              qa2 = tr_chunk(b + C::QN, C::NROW, 32 * qb, ob, ci, lane);
-            } else {
-              oa = keyrow_chunk<T>(b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
-              qa2 = keyrow_chunk<T>(b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
-            }
-            dv[ob] = Elt<T>::mma(oa, pc.c[ci], dv[ob]);
-            dk[ob] = Elt<T>::mma(qa2, dsc.c[ci], dk[ob]);
-          }
-        }
-      }
+      };
+      tile_body(masked);
     }
     if (has_next) store_tile(buf ^ 1);
     __syncthreads();
+  };
+  // 16-bit d <= 64: the mask compiled in or out.  d = 128 (whose registers
+  // are full: the branch-free body spills there) and float32: a run-time flag.
+  if constexpr (C::kTr && D <= 64) {
+    for (int t = t_lo; t < ta; ++t) iterate(t, std::true_type{});
+    for (int t = ta; t < tb; ++t) iterate(t, std::false_type{});
+    for (int t = tb; t < t_hi; ++t) iterate(t, std::true_type{});
+  } else {
+    for (int t = t_lo; t < t_hi; ++t) iterate(t, t < ta || t >= tb);
   }
 
   // Epilogue: lane holds column `key`, rows a = 32 ob + 8 g + 4 h + (0..3).
