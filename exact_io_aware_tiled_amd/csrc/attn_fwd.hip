@@ -14,7 +14,7 @@
 // operand of S^T = K Q^T, so the accumulator gives every lane all the scores of
 // ONE query row (16 keys per 32-key block per half-wave): the row max and row
 // sum are in-lane, plus one exchange of the two half-waves (v_permlane32_swap).
-// Key/value tiles of BN keys (128 for 16-bit d <= 64, else 64) stream through
+// Key/value tiles of BN keys (128 for 16-bit d = 64, else 64) stream through
 // LDS, double-buffered: 16-bit tiles with d >= 32 are copied HBM -> LDS
 // directly (global_load_lds_dwordx4, no staging registers); the others are
 // staged one tile ahead in registers.  K is read row-major as the A operand of S^T.
@@ -49,11 +49,11 @@ struct FwdCfg {
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 32 * kWaves;      // query rows per workgroup
-  // Keys per tile.  16-bit d <= 64 streams 128-key tiles: half the barriers
+  // Keys per tile.  16-bit d = 64 streams 128-key tiles: half the barriers
   // and loop overhead per key, four independent 32-key score blocks per tile
   // (4-7 % faster at d = 64 although the 72 KiB of tiles leave room for two
   // workgroups per CU instead of three).
-  static constexpr int BN = (D <= 64 && Elt<T>::kBytes == 2 && !F8) ? 128 : 64;
+  static constexpr int BN = (D == 64 && Elt<T>::kBytes == 2 && !F8) ? 128 : 64;
   static constexpr int DP = D < 32 ? 32 : D;  // value rows padded to whole 32-row blocks
   static constexpr int S = Elt<T>::kBytes;
   static constexpr bool kTr = (S == 2);       // 16-bit: V row-major + transpose reads
