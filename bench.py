@@ -129,9 +129,10 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
-def fp8_cpu_baseline(w, budget_s: float, signs):
+def fp8_cpu_baseline(w, budget_s: float, signs, values: bool = False):
     """The oracle's FP8 path on whole heads: quantize Q and K (rotation and
-    block scales), dequantize, fp64 forward with c / d."""
+    block scales; with `values` also V along the keys), dequantize, fp64
+    forward with c / d."""
     import torch
 
     import oracle
@@ -146,7 +147,10 @@ def fp8_cpu_baseline(w, budget_s: float, signs):
         t0 = time.perf_counter()
         qd = oracle.mx_dequant(*oracle.mx_quant(flat["q"][hh], sg))
         kd = oracle.mx_dequant(*oracle.mx_quant(flat["k"][hh], sg))
-        oracle.fwd(qd[None], kd[None], flat["v"][hh][None], w.c / w.d, w.mask, w.window)
+        vv = flat["v"][hh]
+        if values:
+            vv = oracle.mx_dequant(*oracle.mx_quant(vv.T)).T
+        oracle.fwd(qd[None], kd[None], vv[None], w.c / w.d, w.mask, w.window)
         t_total += time.perf_counter() - t0
         heads += 1
         if t_total >= budget_s:
@@ -157,7 +161,8 @@ def fp8_cpu_baseline(w, budget_s: float, signs):
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"oracle FP8 quantizer + fp64 dense forward, {heads} of {total_heads} heads "
+        "sample": (f"oracle FP8 quantizer{' (Q, K, V)' if values else ' (Q, K)'} + fp64 dense "
+                   f"forward, {heads} of {total_heads} heads "
                    f"of the same workload (n={w.n}, d={w.d}, {w.mask}); {t_total:.2f} s"),
     }
 
@@ -185,6 +190,10 @@ def bench_fp8(args, w):
     ks = torch.empty_like(qs)
     o = torch.empty(B, H, n, dv, dtype=dt, device=dev)
     lse = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    pv8 = bool(args.fp8_values)
+    nt = (n + 63) // 64
+    v8 = torch.empty(B, H, nt, dv, 64, dtype=torch.uint8, device=dev)
+    vs = torch.empty(B, H, nt, dv, 2, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sh = attn._stream_handle(stream)
     dcode, mcode = attn.DTYPE_CODES[dt], attn.MASK_CODES[w.mask]
@@ -199,12 +208,23 @@ def bench_fp8(args, w):
                                scales.data_ptr(), rows, d, dcode, sh))
 
     def fwd8():
-        chk(lib.attn_fwd_fp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
-                             v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, n, d, dv, dcode,
-                             float(w.c) / d, mcode, w.window, sh))
+        if pv8:
+            chk(lib.attn_fwd_fp8_pv(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
+                                    v8.data_ptr(), vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B,
+                                    H, n, d, dv, dcode, float(w.c) / d, mcode, w.window, sh))
+        else:
+            chk(lib.attn_fwd_fp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
+                                 v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, n, d, dv, dcode,
+                                 float(w.c) / d, mcode, w.window, sh))
 
-    kernels = [("quant_q", lambda: quant(q, q8, qs)), ("quant_k", lambda: quant(k, k8, ks)),
-               ("attn_fwd_fp8", fwd8)]
+    def quant_v():
+        chk(lib.attn_quant_fp8_v(v.data_ptr(), v8.data_ptr(), vs.data_ptr(), B * H, n, dv, dcode,
+                                 sh))
+
+    kernels = [("quant_q", lambda: quant(q, q8, qs)), ("quant_k", lambda: quant(k, k8, ks))]
+    if pv8:
+        kernels.append(("quant_v", quant_v))
+    kernels.append(("attn_fwd_fp8", fwd8))
     log(f"bench: fp8 workload {w}")
     K = args.steps
     ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream)
@@ -216,7 +236,8 @@ def bench_fp8(args, w):
     value = conv_fwd / (ms_per_step * 1e-3) / 1e12
     e = 2 if dt != torch.float32 else 4
     qbytes = float(rows * d * (e + 1) + rows * (d // 32) + d)  # read x, signs; write codes, scales
-    work = {"quant_q": ("hbm", qbytes), "quant_k": ("hbm", qbytes),
+    vbytes = float(rows * dv * e + B * H * nt * dv * (64 + 2))  # read V; write the tile layout
+    work = {"quant_q": ("hbm", qbytes), "quant_k": ("hbm", qbytes), "quant_v": ("hbm", vbytes),
             "attn_fwd_fp8": ("mfma", 4.0 * d * pairs)}
     per_kernel = {}
     for name, ms in kern_ms.items():
@@ -226,12 +247,13 @@ def bench_fp8(args, w):
                             ("tflops" if b_ == "mfma" else "gbs"): round(rate, 2)}
     dom = "attn_fwd_fp8"
     achieved = work[dom][1] / (kern_ms[dom] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["fp8"] if pv8 else PEAK_FP8_FWD  # both products on FP8, or S only
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-            "peak": round(PEAK_FP8_FWD, 1), "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP8_FWD, 4), "traffic": load_traffic(dom, w)}
+            "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": None if pv8 else load_traffic(dom, w)}
     if args.copy_calibration:
         copy_calibration(torch, dev, args.copy_calibration)
-    cpu = fp8_cpu_baseline(w, args.cpu_budget, signs) if args.cpu_budget > 0 else None
+    cpu = fp8_cpu_baseline(w, args.cpu_budget, signs, pv8) if args.cpu_budget > 0 else None
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -243,16 +265,19 @@ def bench_fp8(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"fp8-e4m3 scores (E8M0 block scales), {w.dtype} P and V",
+        "dtype": (f"fp8-e4m3 scores, weights and values (E8M0 block scales), {w.dtype} O" if pv8
+                  else f"fp8-e4m3 scores (E8M0 block scales), {w.dtype} P and V"),
         "data": "synthetic (seeded N(0,1) Q, K, V; seeded random signs)",
         "config": {"workload": (f"{w.name}: B={B} H={H} n={n} d=v={d} {w.dtype} {w.mask}, forward "
-                                "with FP8 scores: quantize Q and K + FP8 forward"),
+                                + ("with FP8 scores, weights and values: quantize Q, K and V + FP8 "
+                                   "forward" if pv8 else
+                                   "with FP8 scores: quantize Q and K + FP8 forward")),
                    "global_batch": B, "seq_len": n, "heads": H, "head_dim": d,
                    "mask": w.mask, "parallelism": "none (1 GPU)"},
         "fwd_tflops": round(conv_fwd / (kern_ms[dom] * 1e-3) / 1e12, 2),
         "kernels": per_kernel,
         "roofline": roof,
-        "counters": load_activity(dom, w),
+        "counters": None if pv8 else load_activity(dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -410,6 +435,9 @@ def main():
     ap.add_argument("--seed", type=int, default=1, help="dropout mask seed")
     ap.add_argument("--fp8", action="store_true",
                     help="forward with FP8 scores (attn_quant_fp8 on Q and K, then attn_fwd_fp8)")
+    ap.add_argument("--fp8-values", action="store_true",
+                    help="with --fp8: FP8 weights and values too (attn_quant_fp8_v on V, then "
+                         "attn_fwd_fp8_pv)")
     ap.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
                     help="override a workload field, e.g. --set n=16384 --set mask=none")
     ap.add_argument("--cpu-budget", type=float, default=12.0,

@@ -82,6 +82,11 @@ def load_library():
     lib.attn_fwd_fp8.argtypes = [u8p, u8p, u8p, u8p, vp, vp, vp, i64, i64, i64, i64, i64, c_int,
                                  c_float, c_int, i64, vp]
     lib.attn_fwd_fp8.restype = c_int
+    lib.attn_quant_fp8_v.argtypes = [vp, u8p, u8p, i64, i64, i64, c_int, vp]
+    lib.attn_quant_fp8_v.restype = c_int
+    lib.attn_fwd_fp8_pv.argtypes = [u8p, u8p, u8p, u8p, u8p, u8p, vp, vp, i64, i64, i64, i64, i64,
+                                    c_int, c_float, c_int, i64, vp]
+    lib.attn_fwd_fp8_pv.restype = c_int
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -182,6 +187,51 @@ def attn_fwd_fp8(q, q_scale, k, k_scale, v, scale: float, mask: str = "causal", 
                             v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n, d, dv,
                             DTYPE_CODES[v.dtype], float(scale), MASK_CODES[mask], int(window),
                             _stream_handle(stream)))
+    return out, lse
+
+
+def attn_quant_fp8_v(v, codes=None, scales=None, stream=None):
+    """(codes, scales) of values v [B, H, n, dv] quantized along the keys
+    (attn_quant_fp8_v): uint8 [B, H, nt, dv, 64] and [B, H, nt, dv, 2], nt =
+    ceil(n / 64), in the tile-major key order the FP8 value product reads."""
+    lib = load_library()
+    _require(v, "v")
+    if v.dim() != 4:
+        raise ValueError("expected v of shape [B, H, n, dv]")
+    B, H, n, dv = v.shape
+    nt = (n + 63) // 64
+    if codes is None:
+        codes = torch.empty(B, H, nt, dv, 64, dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.empty(B, H, nt, dv, 2, dtype=torch.uint8, device=v.device)
+    _check(lib.attn_quant_fp8_v(v.data_ptr(), codes.data_ptr(), scales.data_ptr(), B * H, n, dv,
+                                DTYPE_CODES[v.dtype], _stream_handle(stream)))
+    return codes, scales
+
+
+def attn_fwd_fp8_pv(q, q_scale, k, k_scale, v, v_scale, scale: float, mask: str = "causal",
+                    window: int = 0, out=None, lse=None, dtype=torch.bfloat16, stream=None):
+    """O, LSE with FP8 scores and FP8 weights/values (attn_fwd_fp8_pv): q, k,
+    q_scale, k_scale as attn_fwd_fp8; v, v_scale from attn_quant_fp8_v; O in
+    ``dtype`` (float16 or bfloat16)."""
+    lib = load_library()
+    for name, t in (("q", q), ("q_scale", q_scale), ("k", k), ("k_scale", k_scale), ("v", v),
+                    ("v_scale", v_scale)):
+        _require(t, name)
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be uint8")
+    if q.dim() != 4 or v.dim() != 5:
+        raise ValueError("expected q [B, H, n, d] and v [B, H, nt, dv, 64]")
+    B, H, n, d = q.shape
+    dv = v.shape[-2]
+    if out is None:
+        out = torch.empty(B, H, n, dv, dtype=dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd_fp8_pv(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
+                               v.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                               H, n, d, dv, DTYPE_CODES[out.dtype], float(scale), MASK_CODES[mask],
+                               int(window), _stream_handle(stream)))
     return out, lse
 
 

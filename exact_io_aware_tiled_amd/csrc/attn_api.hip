@@ -194,10 +194,70 @@ eiat_status attn_quant_fp8(const void* x, const int8_t* signs, uint8_t* codes, u
   return ok();
 }
 
+eiat_status attn_quant_fp8_v(const void* v, uint8_t* codes, uint8_t* scales, int64_t BH, int64_t n,
+                           int64_t dv, int dtype, void* stream) {
+  if (BH < 0 || n < 0) return fail(EIAT_ERR_INVALID_ARG, "BH and n must be >= 0");
+  if (dv < 1) return fail(EIAT_ERR_INVALID_ARG, "dv must be >= 1");
+  if (dtype != EIAT_F32 && dtype != EIAT_F16 && dtype != EIAT_BF16)
+    return fail(EIAT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dv != 64 && dv != 128)
+    return fail(EIAT_ERR_UNSUPPORTED, "FP8 values: dv %lld has no kernel (64, 128)", (long long)dv);
+  if (n > (int64_t)INT32_MAX - 64) return fail(EIAT_ERR_UNSUPPORTED, "n too large");
+  const int64_t nt = (n + 63) / 64;
+  if (BH > 0 && nt > (int64_t)INT32_MAX / BH) return fail(EIAT_ERR_UNSUPPORTED, "grid too large");
+  if (BH == 0 || n == 0) return ok();
+  if (!v || !codes || !scales) return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(v) || !aligned16(codes) || !aligned16(scales))
+    return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t vb = (size_t)(BH * n * dv) * elem_bytes(dtype), cb = (size_t)(BH * nt * dv * 64),
+               sb = (size_t)(BH * nt * dv * 2);
+  if (overlaps(codes, cb, v, vb) || overlaps(scales, sb, v, vb))
+    return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap inputs");
+  if (overlaps(codes, cb, scales, sb)) return fail(EIAT_ERR_INVALID_ARG, "codes and scales overlap");
+  eiat::QuantVArgs a;
+  a.v = v;
+  a.codes = codes;
+  a.scales = scales;
+  a.bh = BH;
+  a.n = n;
+  a.dv = (int)dv;
+  a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = eiat::launch_quant_fp8_v(a);
+  if (e != hipSuccess) return fail(EIAT_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static eiat_status fwd_fp8_impl(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k,
+                                const uint8_t* k_scale, const void* v, const uint8_t* v_scale,
+                                void* o, float* lse, int64_t B, int64_t H, int64_t n, int64_t d,
+                                int64_t dv, int dtype, float scale, int mask, int64_t window,
+                                void* stream);
+
 eiat_status attn_fwd_fp8(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k,
                          const uint8_t* k_scale, const void* v, void* o, float* lse, int64_t B,
                          int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale,
                          int mask, int64_t window, void* stream) {
+  return fwd_fp8_impl(q, q_scale, k, k_scale, v, nullptr, o, lse, B, H, n, d, dv, dtype, scale,
+                      mask, window, stream);
+}
+
+eiat_status attn_fwd_fp8_pv(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k,
+                            const uint8_t* k_scale, const uint8_t* v, const uint8_t* v_scale,
+                            void* o, float* lse, int64_t B, int64_t H, int64_t n, int64_t d,
+                            int64_t dv, int dtype, float scale, int mask, int64_t window,
+                            void* stream) {
+  if (!v_scale && B > 0 && H > 0 && n > 0)
+    return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
+  return fwd_fp8_impl(q, q_scale, k, k_scale, v, v_scale, o, lse, B, H, n, d, dv, dtype, scale,
+                      mask, window, stream);
+}
+
+static eiat_status fwd_fp8_impl(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k,
+                                const uint8_t* k_scale, const void* v, const uint8_t* v_scale,
+                                void* o, float* lse, int64_t B, int64_t H, int64_t n, int64_t d,
+                                int64_t dv, int dtype, float scale, int mask, int64_t window,
+                                void* stream) {
   bool empty = false;
   float qk_scale = 1.0f;
   int qmode = 0;
@@ -213,17 +273,21 @@ eiat_status attn_fwd_fp8(const uint8_t* q, const uint8_t* q_scale, const uint8_t
   if (empty) return ok();
   if (!q || !q_scale || !k || !k_scale || !v || !o || !lse)
     return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
-  const void* ptrs[7] = {q, q_scale, k, k_scale, v, o, lse};
-  for (int i = 0; i < 7; ++i)
+  const void* ptrs[8] = {q, q_scale, k, k_scale, v, o, lse, v_scale ? v_scale : q};
+  for (int i = 0; i < 8; ++i)
     if (!aligned16(ptrs[i])) return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const int64_t nt = (n + 63) / 64;
   const size_t qb = (size_t)(B * H * n * d), sb = (size_t)(B * H * n * (d / 32)),
-               vb = (size_t)(B * H * n * dv) * elem_bytes(dtype), lb = (size_t)(B * H * n) * 4;
-  const void* ins[5] = {q, q_scale, k, k_scale, v};
-  const size_t insz[5] = {qb, sb, qb, sb, vb};
-  for (int i = 0; i < 5; ++i)
-    if (overlaps(o, vb, ins[i], insz[i]) || overlaps(lse, lb, ins[i], insz[i]))
+               ob = (size_t)(B * H * n * dv) * elem_bytes(dtype), lb = (size_t)(B * H * n) * 4;
+  // values: dtype rows, or (FP8 values) codes and block scales of the tile layout
+  const size_t vb = v_scale ? (size_t)(B * H * nt * dv * 64) : ob;
+  const size_t vsb = v_scale ? (size_t)(B * H * nt * dv * 2) : 0;
+  const void* ins[6] = {q, q_scale, k, k_scale, v, v_scale};
+  const size_t insz[6] = {qb, sb, qb, sb, vb, vsb};
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(o, ob, ins[i], insz[i]) || overlaps(lse, lb, ins[i], insz[i]))
       return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap inputs");
-  if (overlaps(o, vb, lse, lb)) return fail(EIAT_ERR_INVALID_ARG, "o and lse overlap");
+  if (overlaps(o, ob, lse, lb)) return fail(EIAT_ERR_INVALID_ARG, "o and lse overlap");
 
   eiat::FwdArgs a;
   a.q = q;
@@ -242,6 +306,7 @@ eiat_status attn_fwd_fp8(const uint8_t* q, const uint8_t* q_scale, const uint8_t
   a.drop = kNoDrop;
   a.qscale = q_scale;
   a.kscale = k_scale;
+  a.vscale = v_scale;
   a.stream = static_cast<hipStream_t>(stream);
   hipError_t e = eiat::launch_fwd(a);
   if (e != hipSuccess) return fail(EIAT_ERR_HIP, "forward launch: %s", hipGetErrorString(e));

@@ -159,7 +159,96 @@ hipError_t launch_quant_dt(const QuantArgs& a) {
   return a.d == 64 ? launch_quant_t<T, 64>(a) : launch_quant_t<T, 128>(a);
 }
 
+// ---------------------------------------------------------------------------
+// Values for FP8 weights: V quantized along the keys (the contraction index of
+// P V), with the same block rule and codes as the rows above (no rotation: a
+// rotation of V would have to be undone on O).  Layout written, tile-major so
+// that one 64-key tile of V^T is one contiguous block:
+//   codes  [bh][nt][dv][64], nt = ceil(n / 64): row r of tile t holds value
+//          column r for keys 64 t .. 64 t + 63; 32-key block b (0, 1) fills
+//          bytes 32 b .. 32 b + 31, key 64 t + 32 b + 8 g + 4 h + i (g, i in
+//          0..3, h in 0..1) at byte 32 b + 16 h + 4 g + i -- the order in which
+//          a lane of the score accumulator holds its keys, so that each lane's
+//          16 bytes of a block are contiguous;
+//   scales [bh][nt][dv][2]: the E8M0 scale of each 32-key block.
+// Keys past n count as zero (code 0; a block with no key below n has e = 0).
+// One workgroup per (head, tile): the tile goes through LDS, then thread
+// (r, b) quantizes one 32-key block of column r.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline float lds_elem(const char* p) {
+  if constexpr (__is_same(T, __bf16))
+    return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
+  else if constexpr (__is_same(T, _Float16))
+    return (float)*reinterpret_cast<const _Float16*>(p);
+  else
+    return *reinterpret_cast<const float*>(p);
+}
+
+template <typename T, int DV>
+__global__ void __launch_bounds__(2 * DV)
+    attn_quant_fp8_v_kernel(const T* __restrict__ V, uint8_t* __restrict__ codes,
+                            uint8_t* __restrict__ scales, int n, int nt) {
+  constexpr int S = Elt<T>::kBytes;
+  constexpr int ROW = DV * S + 16;  // LDS row stride, bytes
+  constexpr int CPR = DV * S / 16;  // 16-byte chunks per key row
+  __shared__ __attribute__((aligned(16))) char tile[64 * ROW];
+  const int bh = blockIdx.x / nt, t = blockIdx.x % nt;
+  const int tid = threadIdx.x;
+  const char* src = reinterpret_cast<const char*>(V) + ((int64_t)bh * n + (int64_t)t * 64) * DV * S;
+  for (int c = tid; c < 64 * CPR; c += 2 * DV) {
+    const int row = c / CPR, col = c % CPR;
+    u32x4 w = zero4();
+    if (t * 64 + row < n) w = ldg16(src + (int64_t)row * DV * S + col * 16);
+    *reinterpret_cast<u32x4*>(tile + row * ROW + col * 16) = w;
+  }
+  __syncthreads();
+  const int r = tid % DV, blk = tid / DV;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 32; ++p) {
+    const int key = 32 * blk + 8 * ((p >> 2) & 3) + 4 * (p >> 4) + (p & 3);
+    v[p] = lds_elem<T>(tile + key * ROW + r * S);
+    amax = fmaxf(amax, fabsf(v[p]));
+  }
+  const int e = block_exponent(amax);
+  const float inv = pow2_neg(e);
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * inv, v[4 * q + 1] * inv, 0, false);
+    w[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * inv, v[4 * q + 3] * inv, x, true);
+  }
+  const int64_t rowidx = ((int64_t)bh * nt + t) * DV + r;
+  u32x4 lo = {w[0], w[1], w[2], w[3]}, hi = {w[4], w[5], w[6], w[7]};
+  *reinterpret_cast<u32x4*>(codes + rowidx * 64 + 32 * blk) = lo;
+  *reinterpret_cast<u32x4*>(codes + rowidx * 64 + 32 * blk + 16) = hi;
+  scales[rowidx * 2 + blk] = (uint8_t)(e + 127);
+}
+
+template <typename T, int DV>
+hipError_t launch_quant_v_t(const QuantVArgs& a) {
+  const int nt = (int)((a.n + 63) / 64);
+  hipLaunchKernelGGL((attn_quant_fp8_v_kernel<T, DV>), dim3((unsigned)(a.bh * nt)), dim3(2 * DV),
+                     0, a.stream, static_cast<const T*>(a.v), a.codes, a.scales, (int)a.n, nt);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_quant_v_dt(const QuantVArgs& a) {
+  return a.dv == 64 ? launch_quant_v_t<T, 64>(a) : launch_quant_v_t<T, 128>(a);
+}
+
 }  // namespace
+
+hipError_t launch_quant_fp8_v(const QuantVArgs& a) {
+  switch (a.dtype) {
+    case 0: return launch_quant_v_dt<float>(a);
+    case 1: return launch_quant_v_dt<_Float16>(a);
+    default: return launch_quant_v_dt<__bf16>(a);
+  }
+}
 
 hipError_t launch_quant_fp8(const QuantArgs& a) {
   switch (a.dtype) {

@@ -40,7 +40,9 @@
 
 namespace eiat {
 
-template <typename T, int D, bool F8 = false>
+// F8: 0 16-bit (or float32) scores; 1 FP8 scores; 2 FP8 scores and FP8 weights
+// and values (V in the tile-major layout of attn_quant_fp8_v).
+template <typename T, int D, int F8 = 0>
 struct FwdCfg {
   // 4 waves (128 query rows) share each K/V tile.  At 16-bit d = 128 this beat
   // 8 waves (256 rows, half the K/V loads per row) on every measured shape:
@@ -60,9 +62,9 @@ struct FwdCfg {
   static constexpr int KS = F8 ? 1 : S;       // bytes per Q / K element (FP8 scores: 1)
   static constexpr int KROW = D * KS + 16;    // K tile row stride in LDS (bytes), padded
   // V tile: row-major [BN][DP] (16-bit) or transposed [DP][BN] (float32)
-  static constexpr int VROW = kTr ? DP * S + 16 : BN * S + 16;
+  static constexpr int VROW = F8 == 2 ? 64 + 16 : (kTr ? DP * S + 16 : BN * S + 16);
   static constexpr int KBYTES = BN * KROW;
-  static constexpr int VBYTES = (kTr ? BN : DP) * VROW;
+  static constexpr int VBYTES = (kTr && F8 != 2 ? BN : DP) * VROW;
   static constexpr int NCH = D * S / 32;      // d-chunks per 32x32 product (both halves)
   static constexpr int NQF = F8 ? D / 32 : NCH;  // 16-byte Q chunks per lane
   static constexpr int NOB = DP / 32;         // 32-row blocks of O^T
@@ -88,14 +90,15 @@ struct FwdCfg {
       S == 4 ? (D >= 128 ? 1 : 2) : ((D >= 128 || !__is_same(T, __bf16)) ? 2 : 3);
 };
 
-template <typename T, int D, int MASK, bool DROP, bool F8>
+template <typename T, int D, int MASK, bool DROP, int F8>
 __global__ void
     __attribute__((amdgpu_flat_work_group_size(1, FwdCfg<T, D, F8>::kThreads),
                    amdgpu_waves_per_eu(FwdCfg<T, D, F8>::kMinWaves, 8)))
     attn_fwd_kernel(const void* __restrict__ Q, const void* __restrict__ K, const T* __restrict__ V,
                     T* __restrict__ O, float* __restrict__ LSE, int n, int bh_count,
                     int num_qtiles, int window, float qk_scale, int qmode, DropParams dp,
-                    const uint8_t* __restrict__ Qsc, const uint8_t* __restrict__ Ksc) {
+                    const uint8_t* __restrict__ Qsc, const uint8_t* __restrict__ Ksc,
+                    const uint8_t* __restrict__ Vsc) {
   using C = FwdCfg<T, D, F8>;
   constexpr int BN = C::BN;
   // LDS: two K buffers, then two V buffers.  K runs one tile ahead of V.
@@ -122,7 +125,10 @@ __global__ void
   const int64_t head = (int64_t)bh * n;
   const char* Qh = reinterpret_cast<const char*>(Q) + head * D * C::KS;
   const char* Kh = reinterpret_cast<const char*>(K) + head * D * C::KS;
-  const char* Vh = reinterpret_cast<const char*>(V + head * D);
+  // FP8 values: tile t of this head's V^T is D rows of 64 codes at Vh + t D 64.
+  const int v_tiles = (n + 63) / 64;
+  const char* Vh = F8 == 2 ? reinterpret_cast<const char*>(V) + (int64_t)bh * v_tiles * D * 64
+                           : reinterpret_cast<const char*>(V + head * D);
 
   // Key range any row of this workgroup may see; whole tiles outside it are skipped.
   int kend = n;
@@ -197,6 +203,13 @@ __global__ void
   }
 
   TileLoader<BN, C::CPR, C::kWaves> tl;
+  TileLoader<D, 4, C::kWaves> tlv;  // FP8 values: D rows of 64 codes
+  if constexpr (F8 == 2) tlv.init(wave, lane);
+  // FP8 values: scale words of the V^T rows this lane supplies (block h of
+  // rows 32 ob + L % 32), for the tile multiplied next and the one loading.
+  uint32_t vsw[C::NOB], vsw_next[C::NOB];
+#pragma unroll
+  for (int ob = 0; ob < C::NOB; ++ob) vsw[ob] = vsw_next[ob] = 0;
   TileLoader<BN, C::CPRK, C::kWaves> tlk;
   if constexpr (C::kDirect) {
     tl.init(wave, lane);
@@ -237,6 +250,14 @@ __global__ void
   };
   auto load_v = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
+    if constexpr (F8 == 2) {
+      tlv.load(vbuf(t), Vh + (int64_t)t * D * 64, 0, D, wave, lane);
+      const uint8_t* vs = Vsc + ((int64_t)bh * v_tiles + t) * D * 2;
+#pragma unroll
+      for (int ob = 0; ob < C::NOB; ++ob)
+        vsw_next[ob] = (uint32_t)*reinterpret_cast<const uint16_t*>(vs + (32 * ob + l32) * 2) >> (8 * h);
+      return;
+    }
     if constexpr (C::kDirect) {
       tl.load(vbuf(t), Vh, j0, n, wave, lane);
       return;
@@ -361,6 +382,39 @@ __global__ void
   };
   auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use) __attribute__((always_inline)) {
     const char* vb = vbuf(t);
+    if constexpr (F8 == 2) {
+      // FP8 weights: P rounded to e4m3 with a unit scale (P <= 2^8 < 448),
+      // the lane's 16 keys of each 32-key block in accumulator order, which is
+      // the byte order of the V^T codes; one block-scaled MFMA per 64 keys and
+      // 32 value rows.  l sums the unrounded float32 weights.
+      static_assert(C::NSB == 2, "FP8 values: 64-key tiles");
+      u32x4 pk[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
+        float ts[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ts[e] = s[sb][e] + s[sb][e + 8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ts[e] += ts[e + 4];
+        l_run += (ts[0] + ts[1]) + (ts[2] + ts[3]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[sb][4 * q], s[sb][4 * q + 1], 0, false);
+          pk[sb][q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s[sb][4 * q + 2], s[sb][4 * q + 3],
+                                                                lo, true);
+        }
+      }
+#pragma unroll
+      for (int ob = 0; ob < C::NOB; ++ob) {
+        const char* vr = vb + (32 * ob + l32) * C::VROW + 16 * h;
+        o[ob] = mma_fp8<0>(*reinterpret_cast<const u32x4*>(vr),
+                           *reinterpret_cast<const u32x4*>(vr + 32), pk[0], pk[1], vsw[ob],
+                           0x7F7F7F7Fu, o[ob]);
+      }
+      return;
+    }
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
@@ -405,9 +459,13 @@ __global__ void
   f32x16 sc[C::kDoubleS ? 2 : 1][C::NSB];
   // FP8: the K scale words loaded with a tile become current for its product
   auto advance_ksw = [&]() __attribute__((always_inline)) {
-    if constexpr (F8) {
+    if constexpr (F8 != 0) {
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) ksw[sb] = ksw_next[sb];
+    }
+    if constexpr (F8 == 2) {
+#pragma unroll
+      for (int ob = 0; ob < C::NOB; ++ob) vsw[ob] = vsw_next[ob];
     }
   };
   load_k(t_lo);
@@ -491,7 +549,7 @@ __global__ void
   }
 }
 
-template <typename T, int D, int MASK, bool DROP, bool F8>
+template <typename T, int D, int MASK, bool DROP, int F8>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdCfg<T, D, F8>;
   const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
@@ -499,17 +557,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, MASK, DROP, F8>), dim3((unsigned)blocks),
                      dim3(C::kThreads), 0, a.stream, a.q, a.k, static_cast<const T*>(a.v),
                      static_cast<T*>(a.o), a.lse, (int)a.n, (int)a.bh, num_qtiles, (int)a.window,
-                     a.qk_scale, a.qmode, a.drop, a.qscale, a.kscale);
+                     a.qk_scale, a.qmode, a.drop, a.qscale, a.kscale, a.vscale);
   return hipGetLastError();
 }
 
 template <typename T, int D, int MASK>
 static hipError_t launch_fwd_m(const FwdArgs& a) {
   if constexpr (D >= 64 && Elt<T>::kBytes == 2) {
-    if (a.qscale) return launch_fwd_t<T, D, MASK, false, true>(a);
+    if (a.vscale) return launch_fwd_t<T, D, MASK, false, 2>(a);
+    if (a.qscale) return launch_fwd_t<T, D, MASK, false, 1>(a);
   }
-  return a.drop.thr > 0 ? launch_fwd_t<T, D, MASK, true, false>(a)
-                        : launch_fwd_t<T, D, MASK, false, false>(a);
+  return a.drop.thr > 0 ? launch_fwd_t<T, D, MASK, true, 0>(a)
+                        : launch_fwd_t<T, D, MASK, false, 0>(a);
 }
 
 template <typename T, int D>

@@ -35,6 +35,9 @@ struct FwdArgs {
   // ([bh][n][d / 32]); v, o stay in dtype (16-bit); d is 64 or 128.
   const uint8_t* qscale = nullptr;
   const uint8_t* kscale = nullptr;
+  // FP8 weights and values as well (requires qscale): v holds the codes of
+  // attn_quant_fp8_v's layout and vscale its block scales; o is dtype.
+  const uint8_t* vscale = nullptr;
   hipStream_t stream;
 };
 
@@ -95,11 +98,24 @@ struct QuantArgs {
   hipStream_t stream;
 };
 
+// Values for FP8 weights: V quantized along the keys into the tile-major
+// layout the FP8 value product reads (see attn_fp8.hip).
+struct QuantVArgs {
+  const void* v;          // [bh][n][dv], dtype
+  uint8_t* codes;         // [bh][ceil(n / 64)][dv][64]
+  uint8_t* scales;        // [bh][ceil(n / 64)][dv][2]
+  int64_t bh, n;
+  int dv;                 // 64 or 128
+  int dtype;              // 0 f32, 1 f16, 2 bf16
+  hipStream_t stream;
+};
+
 // Cache ranges per (batch, key/value head) used by the decode kernels.
 int decode_splits(int64_t units, int64_t nk);
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_quant_fp8(const QuantArgs& a);
+hipError_t launch_quant_fp8_v(const QuantVArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 

@@ -52,8 +52,9 @@
 extern "C" {
 #endif
 
-#define EIAT_ABI_VERSION 4  /* 2: adds attn_decode; 3: adds the dropout entry points;
-                               4: adds attn_quant_fp8 and attn_fwd_fp8 */
+#define EIAT_ABI_VERSION 5  /* 2: adds attn_decode; 3: adds the dropout entry points;
+                               4: adds attn_quant_fp8 and attn_fwd_fp8;
+                               5: adds attn_quant_fp8_v and attn_fwd_fp8_pv */
 
 /* Symbols of the shared library (built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -264,6 +265,37 @@ EIAT_API eiat_status attn_fwd_fp8(const uint8_t *q, const uint8_t *q_scale, cons
                                   const uint8_t *k_scale, const void *v, void *o, float *lse,
                                   int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv,
                                   int dtype, float scale, int mask, int64_t window, void *stream);
+
+/*
+ * FP8 weights and values as well (the FP8 throughput figure of the same
+ * section is for both products of FlashAttention-3 in FP8).
+ *
+ * attn_quant_fp8_v writes v [BH][n][dv] (dtype F32, F16 or BF16), quantized
+ * along the keys with the rule of attn_quant_fp8 (32-key blocks of one value
+ * column, E8M0 scale, nearest e4m3 code; no rotation), in a tile-major layout:
+ *   codes  [BH][nt][dv][64] bytes, nt = ceil(n / 64): row r of tile t holds
+ *          value column r for keys 64 t .. 64 t + 63; key 64 t + 32 b + 8 g +
+ *          4 h + i (b, h in 0..1; g, i in 0..3) is at byte 32 b + 16 h + 4 g + i
+ *   scales [BH][nt][dv][2] bytes: scale of block b of row r of tile t
+ * Keys past n count as zero (code 0x00; a block with no key below n has scale
+ * byte 127).  Requires dv in {64, 128} (else EIAT_ERR_UNSUPPORTED).  Device
+ * pointers, 16-byte aligned; outputs must not overlap v or each other.
+ *
+ * attn_fwd_fp8_pv is attn_fwd_fp8 with v, v_scale from attn_quant_fp8_v: the
+ * value product P V runs on the block-scaled FP8 matrix cores too.  The
+ * weights P are rounded to e4m3 for that product (relative error <= 2^-4, or
+ * 2^-10 absolute below 2^-6 in units where the row's largest weight is >= 1);
+ * the normaliser and LSE use the unrounded float32 weights.  O has dtype
+ * (F16 or BF16).  Shapes, masks and errors as attn_fwd_fp8.
+ */
+EIAT_API eiat_status attn_quant_fp8_v(const void *v, uint8_t *codes, uint8_t *scales, int64_t BH,
+                                      int64_t n, int64_t dv, int dtype, void *stream);
+
+EIAT_API eiat_status attn_fwd_fp8_pv(const uint8_t *q, const uint8_t *q_scale, const uint8_t *k,
+                                     const uint8_t *k_scale, const uint8_t *v,
+                                     const uint8_t *v_scale, void *o, float *lse, int64_t B,
+                                     int64_t H, int64_t n, int64_t d, int64_t dv, int dtype,
+                                     float scale, int mask, int64_t window, void *stream);
 
 EIAT_API const char *attn_status_string(int status);
 

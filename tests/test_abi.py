@@ -19,11 +19,12 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
                           "attn_fwd_dropout", "attn_bwd_dropout", "attn_bwd_dropout_stage",
                           "attn_decode", "attn_decode_stage", "attn_decode_workspace_bytes",
-                          "attn_quant_fp8", "attn_fwd_fp8", "attn_status_string",
+                          "attn_quant_fp8", "attn_fwd_fp8", "attn_quant_fp8_v", "attn_fwd_fp8_pv",
+                          "attn_status_string",
                           "attn_last_error", "attn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -221,3 +222,41 @@ def test_fwd_fp8_rejects(lib, kw, code):
 
 def test_fwd_fp8_empty_is_ok_without_gpu(lib):
     assert fwd8(lib, n=0, q=0, qs=0, k=0, ks=0, v=0, o=0, lse=0) == 0
+
+
+def quantv(lib, v=F, codes=F * 2**20, scales=F * 2**21, BH=2, n=100, dv=64, dtype=2):
+    return lib.attn_quant_fp8_v(v, codes, scales, BH, n, dv, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=0), 1), (dict(codes=0), 1), (dict(scales=0), 1), (dict(BH=-1), 1), (dict(n=-3), 1),
+    (dict(dv=0), 1), (dict(dtype=4), 1), (dict(v=F + 8), 1),
+    (dict(codes=F), 1),  # codes overlap v
+    (dict(scales=F * 2**20 + 64), 1),  # scales overlap codes
+    (dict(dv=32), 2), (dict(dv=96), 2),
+])
+def test_quant_fp8_v_rejects(lib, kw, code):
+    assert quantv(lib, **kw) == code
+    assert lib.attn_last_error() != b""
+
+
+def test_quant_fp8_v_empty_is_ok_without_gpu(lib):
+    assert quantv(lib, n=0, v=0, codes=0, scales=0) == 0
+    assert quantv(lib, BH=0, v=0, codes=0, scales=0) == 0
+
+
+def fwd8pv(lib, q=F, qs=F * 2**20, k=F * 2**21, ks=F * 2**22, v=F * 2**23, vs=F * 2**24,
+           o=F * 2**25, lse=F * 2**26, B=1, H=1, n=64, d=64, dv=64, dtype=2, scale=0.125, mask=1,
+           window=0):
+    return lib.attn_fwd_fp8_pv(q, qs, k, ks, v, vs, o, lse, B, H, n, d, dv, dtype, scale, mask,
+                               window, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(vs=0), 1), (dict(v=0), 1), (dict(q=0), 1), (dict(vs=F * 2**24 + 2), 1),
+    (dict(o=F * 2**23 + 1024), 1),  # output overlaps the value codes
+    (dict(dtype=0), 2), (dict(d=16, dv=16), 2), (dict(d=64, dv=128), 2),
+])
+def test_fwd_fp8_pv_rejects(lib, kw, code):
+    assert fwd8pv(lib, **kw) == code
+    assert lib.attn_last_error() != b""

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_tiled_amd import attn_fwd_fp8, attn_quant_fp8
+from exact_io_aware_tiled_amd import attn_fwd_fp8, attn_fwd_fp8_pv, attn_quant_fp8, attn_quant_fp8_v
 from exact_io_aware_tiled_amd.inputs import (FP8_SIGNS_SEED, WORKLOADS, Workload, make_inputs,
                                              make_signs)
 from helpers import announce, check_fwd_fp8, fp8_score_slack, sample_rows, to64
@@ -215,3 +215,174 @@ def test_rotation_lowers_error_against_exact_attention():
         torch.cuda.synchronize()
         errs[rot] = float(np.sqrt(np.mean((to64(o) - exact) ** 2)))
     assert errs[True] < errs[False], errs
+
+
+# ---------------------------------------------------------------------------
+# FP8 weights and values (attn_quant_fp8_v, attn_fwd_fp8_pv)
+# ---------------------------------------------------------------------------
+
+def v_tile_layout(cv, sv, n):
+    """The oracle's codes cv [dv][n] and scales sv [dv][ceil(n / 32)] of one head's
+    V^T, arranged as the tile-major layout the C ABI documents: codes [nt][dv][64]
+    with key 64 t + 32 b + 8 g + 4 h + i at byte 32 b + 16 h + 4 g + i, scales
+    [nt][dv][2]; keys past n are code 0, blocks past n scale byte 127."""
+    dv = cv.shape[0]
+    nt = (n + 63) // 64
+    pos = np.arange(64)
+    b, q = pos // 32, pos % 32
+    key_in_tile = 32 * b + 8 * ((q % 16) // 4) + 4 * (q // 16) + q % 4
+    codes = np.zeros((nt, dv, 64), dtype=np.uint8)
+    for t in range(nt):
+        keys = 64 * t + key_in_tile
+        ok = keys < n
+        codes[t][:, ok] = cv[:, keys[ok]]
+    scales = np.full((nt, dv, 2), 127, dtype=np.uint8)
+    nb = sv.shape[1]
+    for t in range(nt):
+        for bb in range(2):
+            if 2 * t + bb < nb:
+                scales[t, :, bb] = sv[:, 2 * t + bb]
+    return codes, scales
+
+
+def oracle_v(v64):
+    """Per head: the oracle's block-scaled codes of V along the keys, their tile
+    layout, and the dequantized V.  v64 [nh, n, dv] float64."""
+    out_c, out_s, vd = [], [], []
+    n = v64.shape[1]
+    for hh in range(v64.shape[0]):
+        cv, sv = oracle.mx_quant(v64[hh].T)
+        c, s = v_tile_layout(cv, sv, n)
+        out_c.append(c)
+        out_s.append(s)
+        vd.append(oracle.mx_dequant(cv, sv).T)
+    return np.stack(out_c), np.stack(out_s), np.stack(vd)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("n", [1, 65, 200, 256])
+def test_quant_v_codes_exact(dt, dv, n):
+    rng = np.random.default_rng(n + dv)
+    v = rng.standard_normal((2, 3, n, dv)) * np.exp2(rng.uniform(-8, 8, (2, 3, 1, dv)))
+    v[0, 0, :, 5] = 0.0  # a zero column
+    vt = torch.from_numpy(v).to(DT[dt])
+    announce(f"attn_quant_fp8_v {dt} dv={dv} n={n}")
+    codes, scales = attn_quant_fp8_v(vt.to(DEV))
+    torch.cuda.synchronize()
+    rc, rs, _ = oracle_v(to64(vt).reshape(6, n, dv))
+    nt = (n + 63) // 64
+    assert codes.shape == (2, 3, nt, dv, 64) and scales.shape == (2, 3, nt, dv, 2)
+    assert np.array_equal(scales.cpu().numpy().reshape(rs.shape), rs)
+    assert np.array_equal(codes.cpu().numpy().reshape(rc.shape), rc)
+
+
+def pv_bound(qd, kd, vd, c, mask, win, lref):
+    """Per element, the effect of rounding the weights to e4m3 on O (rows of
+    one head): 2^-4 sum_j w_ij |V_jc| + 2^-10 e^(m_i - LSE_i) sum_{j in A_i} |V_jc|,
+    m_i the row's largest score.  The kernel's weights are 2^(x - m'), m' <= m_i,
+    rounded with error <= 2^-4 p + 2^-10; its normaliser is the unrounded sum,
+    at least e^(LSE_i - m_i)."""
+    n = qd.shape[0]
+    s = c * (qd @ kd.T)
+    i, j = np.arange(n)[:, None], np.arange(kd.shape[0])[None, :]
+    allowed = np.ones(s.shape, dtype=bool)
+    if mask != "none":
+        allowed &= j <= i
+    if mask == "window":
+        allowed &= j > i - win
+    m = np.where(allowed, s, -np.inf).max(axis=1)
+    wabs, _, _, _ = oracle.fwd(qd[None], kd[None], np.abs(vd)[None], c, mask, win)
+    vabs = allowed.astype(np.float64) @ np.abs(vd)
+    return 2.0 ** -4 * wabs[0] + 2.0 ** -10 * np.exp(m - lref)[:, None] * vabs
+
+
+def check_pv(o, lse, y, lref, qd, kd, vd, c, mask, win, dtype, what):
+    o64, l64 = to64(o).reshape(y.shape), to64(lse).reshape(lref.shape)
+    nh = qd.shape[0]
+    for hh in range(nh):
+        slack = fp8_score_slack(qd[hh], kd[hh], c)
+        pvb = pv_bound(qd[hh], kd[hh], vd[hh], c, mask, win, lref[hh])
+        vmax = float(np.abs(vd[hh]).max(initial=0.0))
+        err = np.abs(o64[hh] - y[hh])
+        bound = 2e-2 + np.expm1(2 * slack)[:, None] * vmax + pvb
+        assert np.all(err <= bound), f"{what} head {hh}: O err {err.max():.3g}, worst margin " \
+            f"{(err - bound).max():.3g}"
+        assert np.all(np.abs(l64[hh] - lref[hh]) <= 1e-3 + slack), f"{what} head {hh}: LSE"
+        # the bound is a worst case (every rounding in one direction): the mean
+        # error sits well inside it
+        assert err.mean() <= 0.25 * bound.mean(), f"{what} head {hh}: mean error {err.mean():.3g}"
+
+
+PV_SMALL = [(dt, d, mask, win) for dt in ("f16", "bf16") for d in (64, 128)
+            for mask, win in (("none", 0), ("causal", 0), ("window", 50))]
+
+
+@pytest.mark.parametrize("dt,d,mask,win", PV_SMALL)
+def test_fwd_fp8_pv_small(dt, d, mask, win):
+    """n = 200, 3 heads, rotated Q and K: the oracle's codes of Q, K and V uploaded,
+    O against the oracle's attention of the dequantized rows."""
+    w = Workload("fp8pv", 1, 3, 200, d, d, dt, mask, window=win, seed=47)
+    inp = make_inputs(w)
+    codes, qd, kd = oracle_inputs(inp, d, True)
+    vc, vs, vd = oracle_v(to64(inp["v"]).reshape(3, 200, d))
+    c_eff = w.c / d
+    cq, sq, ck, sk = (torch.from_numpy(a).to(DEV) for a in codes)
+    announce(f"attn_fwd_fp8_pv {w}")
+    o, lse = attn_fwd_fp8_pv(cq, sq, ck, sk, torch.from_numpy(vc.reshape(1, 3, *vc.shape[1:])).to(DEV),
+                             torch.from_numpy(vs.reshape(1, 3, *vs.shape[1:])).to(DEV), c_eff, mask,
+                             win, dtype=DT[dt])
+    torch.cuda.synchronize()
+    qd3, kd3 = qd.reshape(3, 200, d), kd.reshape(3, 200, d)
+    y, _, _, lref = oracle.fwd(qd3, kd3, vd, c_eff, mask, win)
+    check_pv(o, lse, y, lref, qd3, kd3, vd, c_eff, mask, win, DT[dt], w.name)
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 129])
+def test_fwd_fp8_pv_edges(n):
+    w = Workload("fp8pve", 1, 2, n, 64, 64, "bf16", "causal", seed=48)
+    inp = make_inputs(w)
+    codes, qd, kd = oracle_inputs(inp, 64, True)
+    vc, vs, vd = oracle_v(to64(inp["v"]).reshape(2, n, 64))
+    cq, sq, ck, sk = (torch.from_numpy(a).to(DEV) for a in codes)
+    announce(f"attn_fwd_fp8_pv n={n}")
+    o, lse = attn_fwd_fp8_pv(cq, sq, ck, sk, torch.from_numpy(vc[None]).to(DEV),
+                             torch.from_numpy(vs[None]).to(DEV), w.c / 64, "causal")
+    torch.cuda.synchronize()
+    qd2, kd2 = qd.reshape(2, n, 64), kd.reshape(2, n, 64)
+    y, _, _, lref = oracle.fwd(qd2, kd2, vd, w.c / 64, "causal")
+    check_pv(o, lse, y, lref, qd2, kd2, vd, w.c / 64, "causal", 0, torch.bfloat16, f"n={n}")
+
+
+@pytest.mark.parametrize("name", ["page_d64", "page_d128"])
+def test_fwd_fp8_pv_full_size(name):
+    """GPU quantizers then the FP8-value forward at the page shape; V's codes of
+    two heads checked whole, sampled rows of every fifth head against the oracle."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    d = w.d
+    signs = make_signs(d, FP8_SIGNS_SEED)
+    announce(f"attn_fwd_fp8_pv full size {w}")
+    q8, qs = attn_quant_fp8(inp["q"].to(DEV), signs.to(DEV))
+    k8, ks = attn_quant_fp8(inp["k"].to(DEV), signs.to(DEV))
+    v8, vs = attn_quant_fp8_v(inp["v"].to(DEV))
+    o, lse = attn_fwd_fp8_pv(q8, qs, k8, ks, v8, vs, w.c / d, "causal")
+    torch.cuda.synchronize()
+    q8c, qsc, k8c, ksc = (t.cpu().numpy() for t in (q8, qs, k8, ks))
+    v8c, vsc = v8.cpu().numpy(), vs.cpu().numpy()
+    rows = sample_rows(w.n, 40, 9, must=(0, 1, 63, 64, 4095))
+    for h in range(0, 32, 5):
+        rc, rs, vd = oracle_v(to64(inp["v"][0, h:h + 1]))
+        if h in (0, 30):
+            assert np.array_equal(v8c[0, h], rc[0]) and np.array_equal(vsc[0, h], rs[0])
+        qd = oracle.mx_dequant(q8c[0, h], qsc[0, h])
+        kd = oracle.mx_dequant(k8c[0, h], ksc[0, h])
+        y, _, _, lref = oracle.fwd(qd, kd, vd[0], w.c / d, "causal", rows=rows)
+        slack = fp8_score_slack(qd[rows], kd, w.c / d)
+        pvb = pv_bound(qd, kd, vd[0], w.c / d, "causal", 0,
+                       oracle.fwd(qd, kd, vd[0], w.c / d, "causal")[3])[rows]
+        err = np.abs(to64(o[0, h, rows]) - y)
+        bound = 2e-2 + np.expm1(2 * slack)[:, None] * float(np.abs(vd).max()) + pvb
+        assert np.all(err <= bound), f"h={h}: O err {err.max():.3g}"
+        assert np.all(np.abs(to64(lse[0, h, rows]) - lref) <= 1e-3 + slack), f"h={h}: LSE"
+        assert err.mean() <= 0.25 * bound.mean()
