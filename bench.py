@@ -224,7 +224,8 @@ def bench_fp8(args, w):
     kernels = [("quant_q", lambda: quant(q, q8, qs)), ("quant_k", lambda: quant(k, k8, ks))]
     if pv8:
         kernels.append(("quant_v", quant_v))
-    kernels.append(("attn_fwd_fp8", fwd8))
+    fwd_name = "attn_fwd_fp8_pv" if pv8 else "attn_fwd_fp8"
+    kernels.append((fwd_name, fwd8))
     log(f"bench: fp8 workload {w}")
     K = args.steps
     ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream)
@@ -238,19 +239,19 @@ def bench_fp8(args, w):
     qbytes = float(rows * d * (e + 1) + rows * (d // 32) + d)  # read x, signs; write codes, scales
     vbytes = float(rows * dv * e + B * H * nt * dv * (64 + 2))  # read V; write the tile layout
     work = {"quant_q": ("hbm", qbytes), "quant_k": ("hbm", qbytes), "quant_v": ("hbm", vbytes),
-            "attn_fwd_fp8": ("mfma", 4.0 * d * pairs)}
+            fwd_name: ("mfma", 4.0 * d * pairs)}
     per_kernel = {}
     for name, ms in kern_ms.items():
         b_, amt = work[name]
         rate = amt / (ms * 1e-3) / (1e12 if b_ == "mfma" else 1e9)
         per_kernel[name] = {"ms": round(ms, 4), "bound": b_,
                             ("tflops" if b_ == "mfma" else "gbs"): round(rate, 2)}
-    dom = "attn_fwd_fp8"
+    dom = fwd_name
     achieved = work[dom][1] / (kern_ms[dom] * 1e-3) / 1e12
     peak = PEAK_TFLOPS["fp8"] if pv8 else PEAK_FP8_FWD  # both products on FP8, or S only
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
             "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": None if pv8 else load_traffic(dom, w)}
+            "traffic": load_traffic(dom, w)}
     if args.copy_calibration:
         copy_calibration(torch, dev, args.copy_calibration)
     cpu = fp8_cpu_baseline(w, args.cpu_budget, signs, pv8) if args.cpu_budget > 0 else None
@@ -277,7 +278,7 @@ def bench_fp8(args, w):
         "fwd_tflops": round(conv_fwd / (kern_ms[dom] * 1e-3) / 1e12, 2),
         "kernels": per_kernel,
         "roofline": roof,
-        "counters": None if pv8 else load_activity(dom, w),
+        "counters": load_activity(dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
