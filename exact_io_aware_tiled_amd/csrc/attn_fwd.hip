@@ -33,6 +33,13 @@
 //
 // Blocks with no allowed key are not visited (causal / window tile ranges) and
 // the per-element mask is applied only in blocks that straddle a boundary.
+//
+// FP8 modes (template F8; webturing.com.tr Principia, "Bellek Duvarinin
+// Fizigi", section on FlashAttention-3): 1 forms S from e4m3 Q and K codes
+// with E8M0 block scales on the block-scaled FP8 MFMA (K = 64 per
+// instruction, the scales applied inside it); 2 also rounds P to e4m3 and
+// forms O^T += V^T P^T from the V^T codes of attn_quant_fp8_v.  The softmax
+// between the two products is the same in every mode.
 #include <type_traits>
 
 #include "attn_device.h"
