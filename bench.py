@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -65,10 +66,15 @@ def convention_pairs(n: int, mask: str, window: int) -> float:
 
 
 def sources_digest() -> str:
+    """Hash of the kernel sources with comments removed: a change to the code
+    invalidates the committed counter summaries, a change to a comment does not."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "exact_io_aware_tiled_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_io_aware_tiled_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(line.rstrip() for line in text.splitlines() if line.strip()).encode())
     return h.hexdigest()[:16]
 
 
