@@ -232,7 +232,7 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
 #pragma unroll
   for (int i0 = 0; i0 < kInstr; i0 += WAVES) {
     const int i = i0 + wave;
-    if (kInstr % WAVES == 0 || i < kInstr) {
+    if (i0 + WAVES <= kInstr || i < kInstr) {  // wave < WAVES
       const int slot = 64 * i + lane;
       if (kSlots % 64 == 0 || slot < kSlots) {
         const int row = slot / (C + 1), c = slot % (C + 1);
@@ -244,12 +244,12 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
   }
 }
 
-// The same copy for tiles whose rows all lie below n, with the cheaper
-// addressing form of the direct load: a wave-uniform 64-bit base in SGPRs
-// (the tile's first row) plus a per-lane 32-bit offset that depends only on
-// the lane's slot and is computed once (init).  Per tile only scalar
-// arithmetic changes; load() falls back to tile_to_lds for a tile that runs
-// past row n - 1.  `wave` must be wave-uniform (e.g. from readfirstlane).
+// The same copy with the cheaper addressing form of the direct load: a
+// wave-uniform 64-bit base in SGPRs (the tile's first row) plus a per-lane
+// 32-bit offset that depends only on the lane's slot and is computed once
+// (init).  Per tile only scalar arithmetic and one min per instruction (the
+// clamp of a tile that runs past row n - 1) change.  `wave` must be
+// wave-uniform (e.g. from readfirstlane).
 template <int R, int C, int WAVES>
 struct TileLoader {
   static constexpr int kSlots = R * (C + 1);
@@ -268,27 +268,41 @@ struct TileLoader {
 
   __device__ inline void load(char* lds_tile, const char* gbase, int r0, int n, int wave,
                               int lane) const {
-    if (r0 + R > n) {
-      tile_to_lds<R, C, WAVES>(lds_tile, gbase, r0, n, wave, lane);
-      return;
-    }
     const char* g = gbase + (int64_t)r0 * (C * 16);
     typedef char __attribute__((address_space(3)))* lds_char_t;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = k * WAVES + wave;
-      if (kInstr % WAVES == 0 || i < kInstr) {
+    // One scalar base per call (this wave's first 1 KiB of the tile); the
+    // instruction k adds its fixed 1024 WAVES k in the same statement, so no
+    // per-instruction LDS address is kept in a scalar register.
+    const uint32_t m0base = (uint32_t)(uintptr_t)(lds_char_t)(lds_tile + 1024 * wave);
+    // A tile that runs past row n - 1 clamps every lane's offset to the last
+    // chunk of that row: rows past n then hold copies of earlier rows' data
+    // (in bounds, finite), which the kernels mask or weight by zero.
+    const uint32_t lim =
+        r0 + R > n ? (uint32_t)((n - r0) * (C * 16) - 16) : 0xFFFFFFFFu;
+    issue<0>(g, m0base, lim, wave, lane);
+  }
+
+ private:
+  template <int K>
+  __device__ inline void issue(const char* g, uint32_t m0base, uint32_t lim, int wave,
+                               int lane) const {
+    if constexpr (K < kPer) {
+      const int i = K * WAVES + wave;
+      // (kPer - 1) WAVES < kInstr, so only the last instruction index can be
+      // past the end for some waves (wave < WAVES)
+      if (K + 1 < kPer || kInstr % WAVES == 0 || i < kInstr) {
         if (kSlots % 64 == 0 || 64 * i + lane < kSlots) {
-          const uint32_t m0v = (uint32_t)(uintptr_t)(lds_char_t)(lds_tile + 1024 * i);
+          const uint32_t o = min(off[K], lim);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-          asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+          asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                        :
-                       : "v"(off[k]), "s"(g), "s"(m0v)
-                       : "memory", "m0");
+                       : "v"(o), "s"(g), "s"(m0base), "n"(1024 * WAVES * K)
+                       : "memory", "m0", "scc");
 #pragma clang diagnostic pop
         }
       }
+      issue<K + 1>(g, m0base, lim, wave, lane);
     }
   }
 };
