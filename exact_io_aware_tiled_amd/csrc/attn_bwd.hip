@@ -341,6 +341,8 @@ __global__ void __launch_bounds__(256)
       auto tile_body = [&](auto masked) __attribute__((always_inline)) {
   #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
+          // scheduling hint: interleave LDS operand reads with the MFMAs
+          __builtin_amdgcn_iglp_opt(0);
           // S = Q K^T and dP - delta = dO V^T - delta for 32 query rows x this
           // wave's 32 keys (without dropout the dP accumulator starts at -delta of
           // its row, so dS = p (dP - delta) needs no subtraction afterwards)
@@ -623,6 +625,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
       if (MASK == 2) straddle = straddle || (j0 < qw0 + 31 - window + 1);
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) {
+        // scheduling hint: interleave LDS operand reads with the MFMAs
+        __builtin_amdgcn_iglp_opt(0);
         // S^T = K Q^T and dP^T = V dO^T: lane holds one query row, 16 keys per half
         // (without dropout dP^T starts at -delta of the lane's row, so
         // dS = p (dP - delta) needs no subtraction afterwards)
