@@ -91,16 +91,24 @@ struct FwdCfg {
   // Two score buffers (next tile's scores issued before this tile's
   // exponentials) where the score MFMAs are long enough to hide the exp work.
   static constexpr bool kDoubleS = D >= 128;
-  // Waves per SIMD the register allocation must allow (4-wave workgroups)
-  // (bf16 at d <= 64 fits three; fp16 needs a few more registers for its sums)
+  // Waves per SIMD the register allocation must allow (4-wave workgroups).
+  // bf16 with 64-key tiles (d = 16, FP8 scores) fits three; fp16 needs a few
+  // more registers for its sums.  128-key tiles hold two workgroups per CU by
+  // their LDS, so two waves: asking for three there left the sliding-window
+  // kernel at one wave per SIMD (264 registers) and 28 % slower.
   static constexpr int kMinWaves =
-      S == 4 ? (D >= 128 ? 1 : 2) : ((D >= 128 || !__is_same(T, __bf16)) ? 2 : 3);
+      S == 4 ? (D >= 128 ? 1 : 2)
+             : ((D >= 128 || BN == 128 || !__is_same(T, __bf16)) ? 2 : 3);
+  // FP8 scores: exactly kMinWaves.  Left free to go higher, the compiler packs
+  // the d = 64 kernels into 128 registers for four waves and spills up to 126
+  // scalar registers into vector lanes inside the loop (4-7 % slower).
+  static constexpr int kMaxWaves = F8 ? kMinWaves : 8;
 };
 
 template <typename T, int D, int MASK, bool DROP, int F8>
 __global__ void
     __attribute__((amdgpu_flat_work_group_size(1, FwdCfg<T, D, F8>::kThreads),
-                   amdgpu_waves_per_eu(FwdCfg<T, D, F8>::kMinWaves, 8)))
+                   amdgpu_waves_per_eu(FwdCfg<T, D, F8>::kMinWaves, FwdCfg<T, D, F8>::kMaxWaves)))
     attn_fwd_kernel(const void* __restrict__ Q, const void* __restrict__ K, const T* __restrict__ V,
                     T* __restrict__ O, float* __restrict__ LSE, int n, int bh_count,
                     int num_qtiles, int window, float qk_scale, int qmode, DropParams dp,
