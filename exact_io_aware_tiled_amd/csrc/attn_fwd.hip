@@ -92,17 +92,17 @@ struct FwdCfg {
   // exponentials) where the score MFMAs are long enough to hide the exp work.
   static constexpr bool kDoubleS = D >= 128;
   // Waves per SIMD the register allocation must allow (4-wave workgroups).
-  // bf16 with 64-key tiles (d = 16, FP8 scores) fits three; fp16 needs a few
+  // 16-bit d = 16 runs four; bf16 FP8-score kernels fit three; fp16 needs a few
   // more registers for its sums.  128-key tiles hold two workgroups per CU by
   // their LDS, so two waves: asking for three there left the sliding-window
   // kernel at one wave per SIMD (264 registers) and 28 % slower.
   static constexpr int kMinWaves =
       S == 4 ? (D >= 128 ? 1 : 2)
-             : ((D >= 128 || BN == 128 || !__is_same(T, __bf16)) ? 2 : 3);
-  // FP8 scores: exactly kMinWaves.  Left free to go higher, the compiler packs
-  // the d = 64 kernels into 128 registers for four waves and spills up to 126
-  // scalar registers into vector lanes inside the loop (4-7 % slower).
-  static constexpr int kMaxWaves = F8 ? kMinWaves : 8;
+             : (D == 16 ? 4 : ((D >= 128 || BN == 128 || !__is_same(T, __bf16)) ? 2 : 3));
+  // FP8 scores and 16-bit d = 16: exactly kMinWaves.  Left free to go higher,
+  // the compiler spilled up to 126 scalar registers into vector lanes inside
+  // the loop (FP8 d = 64: 4-7 % slower; d = 16: 1-5 %).
+  static constexpr int kMaxWaves = (F8 || (D == 16 && S == 2)) ? kMinWaves : 8;
 };
 
 template <typename T, int D, int MASK, bool DROP, int F8>
