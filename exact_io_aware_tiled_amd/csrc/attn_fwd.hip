@@ -368,20 +368,51 @@ __global__ void
   // adds its sum to l and accumulates O^T += V^T P^T.  A tile with no allowed
   // key for some row leaves that row unchanged (its P is 0), as the
   // Algorithm's empty-block skip does.
+  // Boundary tiles: the 32-key blocks [sb_lo, sb_hi) of tile t that hold an
+  // allowed key for at least one row of this wave (wave-uniform).  The others
+  // contribute exactly nothing (every weight 0), so they are not visited.  The
+  // FP8-value product covers two blocks per instruction and keeps them all.
+  int sb_lo = 0, sb_hi = C::NSB;
+  auto block_range = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * BN;
+    int lo = 0, hi = C::NSB;
+    if constexpr (F8 != 2) {
+      const int last = min(n - 1, MASK != 0 ? qw0 + 31 : n - 1) - j0;  // last key any row may see
+      hi = last < 0 ? 0 : min(hi, last / 32 + 1);
+      if constexpr (MASK == 2) {
+        const int first = qw0 - window + 1 - j0;  // first key any row may see
+        if (first > 0) lo = min(hi, first / 32);
+      }
+    }
+    sb_lo = lo;
+    sb_hi = hi;
+  };
+  auto active = [&](int sb, auto masked) __attribute__((always_inline)) -> bool {
+    if constexpr (decltype(masked)::value) return sb >= sb_lo && sb < sb_hi;
+    return true;
+  };
   auto prep_tile = [&](int t, f32x16 (&s)[C::NSB], auto masked) __attribute__((always_inline)) -> float {
     const int j0 = t * BN;
+    float mx = -INFINITY;
     if constexpr (decltype(masked)::value) {
+      block_range(t);
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        if (!active(sb, masked)) continue;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
           if (!key_allowed<MASK>(qrow, j, n, window)) s[sb][e] = -INFINITY;
+          m4[e & 3] = fmaxf(m4[e & 3], s[sb][e]);
         }
+      }
+      mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+    } else {
+      // Block maximum of this row, in units of log2 (c * log2(e) folded in),
+      // as a shallow tree so the reduction is not one long dependency chain.
+      mx = halves_max(tile_max<C::NSB>(s));
     }
-    // Block maximum of this row, in units of log2 (c * log2(e) folded in),
-    // as a shallow tree so the reduction is not one long dependency chain.
-    float mx = halves_max(tile_max<C::NSB>(s));
     const float m_blk = (mx == -INFINITY) ? -INFINITY : mx * qk_scale;
     // Raise the shift (and rescale) only if some row's max grew by more than tau.
     if (wave_any(m_blk > m_run + C::kTau)) {
@@ -395,7 +426,7 @@ __global__ void
     // A row with no allowed key so far keeps the empty summary: shift by 0.
     return (m_run == -INFINITY) ? 0.0f : m_run;
   };
-  auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use) __attribute__((always_inline)) {
+  auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use, auto masked) __attribute__((always_inline)) {
     const char* vb = vbuf(t);
     if constexpr (F8 == 2) {
       // FP8 weights: P rounded to e4m3 with a unit scale (P <= 2^8 < 448),
@@ -432,6 +463,7 @@ __global__ void
     }
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
+      if (!active(sb, masked)) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
       PChunks<T> pc;
@@ -519,9 +551,9 @@ __global__ void
     // t + 1 == t_hi reads a stale buffer; the result is unused
     if constexpr (C::kDoubleS) {
       qk(t + 1, sc[C::kDoubleS ? 1 : 0]);
-      exp_pv_tile(t, sc[0], m_use);
+      exp_pv_tile(t, sc[0], m_use, masked);
     } else {
-      exp_pv_tile(t, sc[0], m_use);
+      exp_pv_tile(t, sc[0], m_use, masked);
       qk(t + 1, sc[0]);
     }
     __builtin_amdgcn_s_setprio(0);
