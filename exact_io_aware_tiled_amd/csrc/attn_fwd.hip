@@ -548,13 +548,23 @@ __global__ void
     // the MFMAs (2-10 % faster on the 16-bit forwards at n = 4096-65536; 2-8 %
     // slower with FP8 scores, so those keep the default schedule).
     if constexpr (F8 == 0) __builtin_amdgcn_iglp_opt(0);
-    // t + 1 == t_hi reads a stale buffer; the result is unused
+    // The next tile's scores.  In the mask-free body t + 1 == t_hi reads a
+    // stale buffer whose result is unused (no branch there, so the score MFMAs
+    // interleave with the exponentials); a boundary tile, which is the last one
+    // of every causal row block, skips them.
+    auto next_scores = [&](f32x16 (&s)[C::NSB]) __attribute__((always_inline)) {
+      if constexpr (decltype(masked)::value) {
+        if (has1) qk(t + 1, s);
+      } else {
+        qk(t + 1, s);
+      }
+    };
     if constexpr (C::kDoubleS) {
-      qk(t + 1, sc[C::kDoubleS ? 1 : 0]);
+      next_scores(sc[C::kDoubleS ? 1 : 0]);
       exp_pv_tile(t, sc[0], m_use, masked);
     } else {
       exp_pv_tile(t, sc[0], m_use, masked);
-      qk(t + 1, sc[0]);
+      next_scores(sc[0]);
     }
     __builtin_amdgcn_s_setprio(0);
     if (has1) store_v(t + 1);
