@@ -368,6 +368,7 @@ __global__ void
   // adds its sum to l and accumulates O^T += V^T P^T.  A tile with no allowed
   // key for some row leaves that row unchanged (its P is 0), as the
   // Algorithm's empty-block skip does.
+  //
   // Boundary tiles: the 32-key blocks [sb_lo, sb_hi) of tile t that hold an
   // allowed key for at least one row of this wave (wave-uniform).  The others
   // contribute exactly nothing (every weight 0), so they are not visited.  The
