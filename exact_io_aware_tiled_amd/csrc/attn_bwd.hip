@@ -264,7 +264,8 @@ __global__ void __launch_bounds__(256)
   TileLoader<BMQ, D * C::S / 16, C::kWaves> tl;
   if constexpr (C::kDirect) tl.init(wave, lane);
   St sq, so;
-  float4 lreg, dreg;  // LSE * log2(e) and delta for 4 rows (threads < BMQ / 4)
+  float4 lreg, dreg;  // LSE and delta of 4 rows as loaded (threads < BMQ / 4)
+  int lrow0 = 0;      // first row of the tile those loads belong to
   u32x4 kreg;         // dropout row keys of the same 4 rows (DROP)
 
   auto load_tile = [&](int t) {
@@ -277,6 +278,11 @@ __global__ void __launch_bounds__(256)
       sq.load(Qh, r0, n, tid);
       so.load(dOh, r0, n, tid);
     }
+    // LSE and delta are only loaded here; they are scaled and stored with the
+    // tile (store_tile), after its loads have been waited for: using them right
+    // after the load would wait for every load issued before them, the tile
+    // prefetch included (vector-memory loads retire in order).
+    lrow0 = r0;
     if (tid < BMQ / 4) {
       float* lr = reinterpret_cast<float*>(&lreg);
       float* dr = reinterpret_cast<float*>(&dreg);
@@ -284,10 +290,8 @@ __global__ void __launch_bounds__(256)
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + 4 * tid + i;
         const int rc = min(r, n - 1);
-        const float lv = LSEh[rc] * kLog2e, dv0 = Dh[rc];
-        // rows past n contribute nothing: p = 2^(-inf) = 0
-        lr[i] = r < n ? lv : INFINITY;
-        dr[i] = r < n ? -dv0 : 0.0f;  // -delta: the dP accumulator starts from it
+        lr[i] = LSEh[rc];
+        dr[i] = Dh[rc];
         if constexpr (DROP) kreg[i] = drop_row_key(dpar, (uint32_t)bh, (uint32_t)r);
       }
     }
@@ -301,8 +305,20 @@ __global__ void __launch_bounds__(256)
       so.store(b + C::ON, b + C::OT, tid);
     }
     if (tid < BMQ / 4) {
-      *reinterpret_cast<float4*>(b + C::LS + 16 * tid) = lreg;
-      *reinterpret_cast<float4*>(b + C::DL + 16 * tid) = dreg;
+      const float* lr = reinterpret_cast<const float*>(&lreg);
+      const float* dr = reinterpret_cast<const float*>(&dreg);
+      float4 ls4, dl4;
+      float* lo = reinterpret_cast<float*>(&ls4);
+      float* dlo = reinterpret_cast<float*>(&dl4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = lrow0 + 4 * tid + i < n;
+        // rows past n contribute nothing: p = 2^(-inf) = 0
+        lo[i] = valid ? lr[i] * kLog2e : INFINITY;
+        dlo[i] = valid ? -dr[i] : 0.0f;  // -delta: the dP accumulator starts from it
+      }
+      *reinterpret_cast<float4*>(b + C::LS + 16 * tid) = ls4;
+      *reinterpret_cast<float4*>(b + C::DL + 16 * tid) = dl4;
       if constexpr (DROP) *reinterpret_cast<u32x4*>(b + C::RK + 16 * tid) = kreg;
     }
   };

@@ -178,11 +178,14 @@ __device__ inline f32x16 mma_fp8(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u32x4 b_hi,
 // A row's E8M0 scale bytes (D / 32 of them at p) as the scale word of half-wave
 // h: byte 2c holds the scale of block 2c + h (chunk c of 64 values).
 template <int D>
-__device__ inline uint32_t scale_word(const uint8_t* p, int h) {
+__device__ inline uint32_t scale_word_raw(const uint8_t* p) {
   static_assert(D == 64 || D == 128, "FP8 scores: d is 64 or 128");
-  const uint32_t w = D == 64 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p)
-                             : *reinterpret_cast<const uint32_t*>(p);
-  return w >> (8 * h);
+  return D == 64 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p)
+                 : *reinterpret_cast<const uint32_t*>(p);
+}
+template <int D>
+__device__ inline uint32_t scale_word(const uint8_t* p, int h) {
+  return scale_word_raw<D>(p) >> (8 * h);
 }
 
 // Negate four e4m3 codes per word: flip the sign of every code with a nonzero

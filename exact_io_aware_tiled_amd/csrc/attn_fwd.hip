@@ -247,7 +247,7 @@ __global__ void
       tlk.load(kbuf(t), Kh, j0, n, wave, lane);
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb)
-        ksw_next[sb] = scale_word<D>(Ksh + (int64_t)min(j0 + 32 * sb + l32, n - 1) * (D / 32), h);
+        ksw_next[sb] = scale_word_raw<D>(Ksh + (int64_t)min(j0 + 32 * sb + l32, n - 1) * (D / 32));
       return;
     } else if constexpr (C::kDirect) {
       tl.load(kbuf(t), Kh, j0, n, wave, lane);
@@ -270,7 +270,7 @@ __global__ void
       const uint8_t* vs = Vsc + ((int64_t)bh * v_tiles + t) * D * 2;
 #pragma unroll
       for (int ob = 0; ob < C::NOB; ++ob)
-        vsw_next[ob] = (uint32_t)*reinterpret_cast<const uint16_t*>(vs + (32 * ob + l32) * 2) >> (8 * h);
+        vsw_next[ob] = (uint32_t)*reinterpret_cast<const uint16_t*>(vs + (32 * ob + l32) * 2);
       return;
     }
     if constexpr (C::kDirect) {
@@ -505,15 +505,19 @@ __global__ void
 
   // Prologue: K_lo, V_lo and K_lo+1 in LDS, S_lo in registers.
   f32x16 sc[C::kDoubleS ? 2 : 1][C::NSB];
-  // FP8: the K scale words loaded with a tile become current for its product
+  // FP8: the K scale words loaded with a tile become current for its product.
+  // They are loaded raw and shifted to this half-wave's bytes only here, after
+  // the tile loads have been waited for: an operation on them right after the
+  // load would wait for every load issued before them, the whole tile prefetch
+  // included (vector-memory loads retire in order).
   auto advance_ksw = [&]() __attribute__((always_inline)) {
     if constexpr (F8 != 0) {
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) ksw[sb] = ksw_next[sb];
+      for (int sb = 0; sb < C::NSB; ++sb) ksw[sb] = ksw_next[sb] >> (8 * h);
     }
     if constexpr (F8 == 2) {
 #pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob) vsw[ob] = vsw_next[ob];
+      for (int ob = 0; ob < C::NOB; ++ob) vsw[ob] = vsw_next[ob] >> (8 * h);
     }
   };
   load_k(t_lo);
@@ -568,8 +572,18 @@ __global__ void
       next_scores(sc[0]);
     }
     __builtin_amdgcn_s_setprio(0);
-    if (has1) store_v(t + 1);
-    if (has2) store_k(t + 2);
+    if constexpr (F8 != 0) {
+      // FP8: one unconditional wait for the direct tile loads.  Behind a branch
+      // the compiler sank this tile's products past the wait (they touch no
+      // memory), which turned the prefetch into a synchronous load (15-17 %
+      // slower FP8-value forward).  The 16-bit kernels keep the branches: there
+      // the products stay ahead of the wait, and the unconditional form measured
+      // 3-12 % slower.
+      wait_tile_loads();
+    } else {
+      if (has1) store_v(t + 1);
+      if (has2) store_k(t + 2);
+    }
     advance_ksw();
     __syncthreads();
     if constexpr (C::kDoubleS) {
