@@ -520,14 +520,24 @@ __global__ void
       for (int ob = 0; ob < C::NOB; ++ob) vsw[ob] = vsw_next[ob] >> (8 * h);
     }
   };
-  load_k(t_lo);
-  load_v(t_lo);
-  store_k(t_lo);
-  store_v(t_lo);
-  advance_ksw();
-  if (t_lo + 1 < t_hi) {
-    load_k(t_lo + 1);
-    store_k(t_lo + 1);
+  if constexpr (C::kDirect && F8 == 0) {
+    // All three tiles in flight together, then one wait (not two in a row).
+    load_k(t_lo);
+    load_v(t_lo);
+    if (t_lo + 1 < t_hi) load_k(t_lo + 1);
+    wait_tile_loads();
+  } else {
+    // Register staging holds one tile at a time; FP8 advances the K scale
+    // words of tile t_lo before those of t_lo + 1 are loaded.
+    load_k(t_lo);
+    load_v(t_lo);
+    store_k(t_lo);
+    store_v(t_lo);
+    advance_ksw();
+    if (t_lo + 1 < t_hi) {
+      load_k(t_lo + 1);
+      store_k(t_lo + 1);
+    }
   }
   __syncthreads();
   qk(t_lo, sc[0]);
