@@ -66,9 +66,12 @@ def convention_pairs(n: int, mask: str, window: int) -> float:
 
 
 def sources_digest() -> str:
-    """Hash of the kernel sources with comments removed: a change to the code
-    invalidates the committed counter summaries, a change to a comment does not."""
+    """Hash of the kernel sources with comments removed, and of the per-source
+    compile flags: a change to the code or to how it is compiled invalidates the
+    committed counter summaries, a change to a comment does not."""
+    from exact_io_aware_tiled_amd import build as _build
     h = hashlib.sha256()
+    h.update(repr(sorted(_build.PER_SOURCE_FLAGS.items())).encode())
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "exact_io_aware_tiled_amd", "csrc", name)) as f:
             text = f.read()
