@@ -560,9 +560,10 @@ __global__ void
     // softmax VALU work fills the gaps rather than delaying them.
     __builtin_amdgcn_s_setprio(1);
     // Scheduling hint for this region: interleave the LDS operand reads with
-    // the MFMAs (2-10 % faster on the 16-bit forwards at n = 4096-65536; 2-8 %
-    // slower with FP8 scores, so those keep the default schedule).
-    if constexpr (F8 == 0) __builtin_amdgcn_iglp_opt(0);
+    // the MFMAs (2-10 % faster on the 16-bit forwards at n = 4096-65536, 1-5 %
+    // on the FP8-value ones and 2-3 % on FP8 scores at d = 128; FP8 scores at
+    // d = 64 measured 3-5 % slower with it and keep the default schedule).
+    if constexpr (!(F8 == 1 && D == 64)) __builtin_amdgcn_iglp_opt(0);
     // The next tile's scores.  In the mask-free body t + 1 == t_hi reads a
     // stale buffer whose result is unused (no branch there, so the score MFMAs
     // interleave with the exponentials); a boundary tile, which is the last one
