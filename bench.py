@@ -3,8 +3,9 @@
 
 A step is one pass of the whole path over one batch of synthetic input that is
 already resident in HBM: the forward (attn_fwd: O and LSE) followed by the
-three steps of the backward (delta, dK/dV, dQ, called through attn_bwd_stage
-so each kernel can be timed on its own).  Default workload: batch 1, 32 heads,
+two kernels of the backward in attn_bwd's order (dQ, which also forms the
+per-row delta, then dK/dV; called through attn_bwd_stage so each kernel can be
+timed on its own).  Default workload: batch 1, 32 heads,
 n = 4096, d = v = 64, bf16, causal, c = 1/8.
 
 Prints ONE JSON line on stdout.  `value` is whole-step algorithmic TFLOP/s with
@@ -524,8 +525,7 @@ def main():
 
     kernels = [("attn_fwd", fwd)]
     if not args.fwd_only:
-        kernels += [("bwd_delta", lambda: bwd_stage(0)), ("bwd_dkdv", lambda: bwd_stage(1)),
-                    ("bwd_dq", lambda: bwd_stage(2))]
+        kernels += [("bwd_dq", lambda: bwd_stage(2)), ("bwd_dkdv", lambda: bwd_stage(1))]
 
     log(f"bench: workload {w}")
     K = args.steps
@@ -541,12 +541,10 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
 
     # algorithmic work per launch of each kernel
-    e = 4 if w.dtype == "f32" else 2
     work = {
         "attn_fwd": ("mfma", 4.0 * d * pairs),      # S and P V
         "bwd_dkdv": ("mfma", 8.0 * d * pairs),      # S, dP, dV, dK
-        "bwd_dq": ("mfma", 6.0 * d * pairs),        # S, dP, dQ
-        "bwd_delta": ("hbm", float(bh * n * (2 * dv * e + 4))),  # read O, dO; write delta
+        "bwd_dq": ("mfma", 6.0 * d * pairs),        # S, dP, dQ (and delta, O . dO per row)
     }
     dom = max(kern_ms, key=kern_ms.get)
     bound, amount = work[dom]

@@ -244,8 +244,9 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "ca
              stage: Optional[int] = None, p_drop: float = 0.0, seed: int = 0):
     """dQ, dK, dV of sum(dO * O) given the forward's O and LSE.
 
-    stage=None runs attn_bwd (all steps); stage 0, 1 or 2 runs attn_bwd_stage
-    (delta into `workspace`; dK and dV; dQ) -- pass the same workspace to all.
+    stage=None runs attn_bwd (dQ with delta, then dK and dV); stage 0, 1 or 2
+    runs attn_bwd_stage (delta into `workspace`; dK and dV, reading delta; dQ,
+    also writing delta) -- pass the same workspace to all.
     p_drop > 0 replays the dropout of attn_fwd(..., p_drop, seed) (same values).
     """
     lib = load_library()

@@ -388,7 +388,7 @@ eiat_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, void* dq, void* dk, void* dvv, void* workspace,
                      size_t workspace_bytes, int64_t B, int64_t H, int64_t n, int64_t d,
                      int64_t dv, int dtype, float scale, int mask, int64_t window, void* stream) {
-  return bwd_impl(7, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H, n, d,
+  return bwd_impl(6, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H, n, d,
                   dv, dtype, scale, mask, window, kNoDrop, stream);
 }
 
@@ -400,7 +400,7 @@ eiat_status attn_bwd_dropout(const void* q, const void* k, const void* v, const 
   eiat::DropParams dp;
   eiat_status s = drop_params(p_drop, seed, &dp);
   if (s != EIAT_OK) return s;
-  return bwd_impl(7, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H, n, d,
+  return bwd_impl(6, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H, n, d,
                   dv, dtype, scale, mask, window, dp, stream);
 }
 

@@ -97,47 +97,57 @@ __device__ inline void zero_pad_rows(char* tr, int tid) {
 // ---------------------------------------------------------------------------
 // 1. delta_i = sum_a dO_ia O_ia
 // ---------------------------------------------------------------------------
+// Dot product of one 16-byte unit of an O row with the same unit of its dO row:
+// fused multiply-adds in element order, starting from zero.  A row's delta is
+// the sum of its units' dots in a fixed tree: unit u is first added to unit
+// u ^ (units / 2), then u ^ (units / 4), ..., and last u ^ 1.  The delta kernel
+// and the dQ kernel both follow it, so they give the same bits.
+template <typename T>
+__device__ inline float unit_dot(const u32x4& a, const u32x4& b) {
+  float acc = 0.0f;
+  if constexpr (Elt<T>::kBytes == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float a0, a1, b0, b1;
+      if constexpr (__is_same(T, __bf16)) {
+        a0 = __uint_as_float(a[w] << 16);
+        a1 = __uint_as_float(a[w] & 0xFFFF0000u);
+        b0 = __uint_as_float(b[w] << 16);
+        b1 = __uint_as_float(b[w] & 0xFFFF0000u);
+      } else {
+        // copy the elements out first: a bit-cast applied directly to a vector
+        // element was compiled into a read of element 0
+        const uint32_t aw = a[w], bw = b[w];
+        const f16x2 ah = __builtin_bit_cast(f16x2, aw), bh = __builtin_bit_cast(f16x2, bw);
+        a0 = (float)ah[0];
+        a1 = (float)ah[1];
+        b0 = (float)bh[0];
+        b1 = (float)bh[1];
+      }
+      acc = __builtin_fmaf(a0, b0, acc);
+      acc = __builtin_fmaf(a1, b1, acc);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = __builtin_fmaf(__uint_as_float(a[w]), __uint_as_float(b[w]), acc);
+  }
+  return acc;
+}
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const T* __restrict__ O,
                                                              const T* __restrict__ dO,
                                                              float* __restrict__ delta,
                                                              int64_t rows) {
   constexpr int S = Elt<T>::kBytes;
-  constexpr int CPR = D * S / 16;  // threads per row (a power of two <= 32)
+  constexpr int CPR = D * S / 16;  // threads (units) per row, a power of two <= 32
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gt / CPR;
   const int col = (int)(gt % CPR);
   float acc = 0.0f;
-  if (row < rows) {
-    u32x4 a = ldg16(reinterpret_cast<const char*>(O) + row * D * S + col * 16);
-    u32x4 b = ldg16(reinterpret_cast<const char*>(dO) + row * D * S + col * 16);
-    if constexpr (S == 2) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float a0, a1, b0, b1;
-        if constexpr (__is_same(T, __bf16)) {
-          a0 = __uint_as_float(a[w] << 16);
-          a1 = __uint_as_float(a[w] & 0xFFFF0000u);
-          b0 = __uint_as_float(b[w] << 16);
-          b1 = __uint_as_float(b[w] & 0xFFFF0000u);
-        } else {
-          // copy the elements out first: a bit-cast applied directly to a vector
-          // element was compiled into a read of element 0
-          const uint32_t aw = a[w], bw = b[w];
-          const f16x2 ah = __builtin_bit_cast(f16x2, aw), bh = __builtin_bit_cast(f16x2, bw);
-          a0 = (float)ah[0];
-          a1 = (float)ah[1];
-          b0 = (float)bh[0];
-          b1 = (float)bh[1];
-        }
-        acc = __builtin_fmaf(a0, b0, acc);
-        acc = __builtin_fmaf(a1, b1, acc);
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc = __builtin_fmaf(__uint_as_float(a[w]), __uint_as_float(b[w]), acc);
-    }
-  }
+  if (row < rows)
+    acc = unit_dot<T>(ldg16(reinterpret_cast<const char*>(O) + row * D * S + col * 16),
+                      ldg16(reinterpret_cast<const char*>(dO) + row * D * S + col * 16));
 #pragma unroll
   for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && col == 0) delta[row] = acc;
@@ -541,9 +551,9 @@ struct DqCfg {
 template <typename T, int D, int MASK, bool DROP>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    T* __restrict__ dQ, int n, int bh_count, int num_qtiles, int window, float qk_scale,
-    int qmode, float scale, DropParams dpar) {
+    const T* __restrict__ dO, const T* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ delta, T* __restrict__ dQ, int n, int bh_count, int num_qtiles,
+    int window, float qk_scale, int qmode, float scale, DropParams dpar) {
   using C = DqCfg<T, D>;
   constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
@@ -575,7 +585,25 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
     if (qmode == 2) qf[c] = zero4();  // c = 0: every score is exactly 0
   }
   const float lse2 = qrow < n ? LSE[head + qrow] * kLog2e : INFINITY;
-  const float dlt = qrow < n ? delta[head + qrow] : 0.0f;
+  // delta of this row from its O and the dO chunks above (unit 2c + h of the
+  // row is chunk c of half h), summed in unit_dot's tree; written out for the
+  // dK/dV kernel.
+  float dlt;
+  {
+    const char* Oh = reinterpret_cast<const char*>(O + head * D);
+    float u[C::NCH];
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+      u[c] = unit_dot<T>(qrow < n ? ldg16(Oh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4(),
+                         of[c]);
+#pragma unroll
+    for (int off = C::NCH / 2; off > 0; off >>= 1)
+#pragma unroll
+      for (int c = 0; c < off; ++c) u[c] += u[c + off];
+    dlt = u[0] + __shfl_xor(u[0], 32, 64);
+    if (qrow >= n) dlt = 0.0f;
+    else if (h == 0) delta[head + qrow] = dlt;
+  }
   // Dropout (DROP): this row's key of the realized mask.
   const uint32_t row_key = DROP ? drop_row_key(dpar, (uint32_t)bh, (uint32_t)qrow) : 0u;
 
@@ -744,6 +772,20 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // dQ (which also writes delta) runs before dK/dV, which reads it
+  if (a.stages & 4) {
+    using C = DqCfg<T, D>;
+    const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK, DROP>),
+                       dim3((unsigned)(num_qtiles * a.bh)), dim3(C::kThreads), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
+                       static_cast<const T*>(a.o), a.lse, a.delta, static_cast<T*>(a.dq),
+                       (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
+                       a.scale, a.drop);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.stages & 2) {
     using C = DkvCfg<T, D>;
     const int num_ktiles = (int)((a.n + C::BNK - 1) / C::BNK);
@@ -753,18 +795,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
                        static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
                        static_cast<T*>(a.dk), static_cast<T*>(a.dv), (int)a.n, (int)a.bh,
                        num_ktiles, (int)a.window, a.qk_scale, a.qmode, a.scale, a.drop);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.stages & 4) {
-    using C = DqCfg<T, D>;
-    const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK, DROP>),
-                       dim3((unsigned)(num_qtiles * a.bh)), dim3(C::kThreads), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                       static_cast<T*>(a.dq), (int)a.n, (int)a.bh, num_qtiles, (int)a.window,
-                       a.qk_scale, a.qmode, a.scale, a.drop);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

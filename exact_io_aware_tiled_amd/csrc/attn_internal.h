@@ -61,7 +61,7 @@ struct BwdArgs {
   float qk_scale;    // as FwdArgs
   int qmode;
   float scale;       // c itself (multiplies dQ and dK)
-  int stages;        // bit 0: delta, bit 1: dK/dV, bit 2: dQ
+  int stages;        // bit 0: delta, bit 1: dK/dV, bit 2: dQ and delta (run before dK/dV)
   DropParams drop;   // the forward's dropout, replayed (thr == 0: none)
   hipStream_t stream;
 };

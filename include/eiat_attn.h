@@ -101,10 +101,11 @@ EIAT_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n);
 
 /*
  * Backward pass: the Algorithm's reverse procedure with the forward's maxima
- * and normalisers frozen (carried here as lse).  First delta_i = sum_a dO_ia O_ia
- * into `workspace`, then one kernel that holds a key/value tile and streams the
- * query tiles that may see it (dK, dV), then one that holds a query tile and
- * streams key/value tiles (dQ).  Each recomputes its score blocks from q, k and
+ * and normalisers frozen (carried here as lse).  First one kernel that holds a
+ * query tile and streams key/value tiles (dQ); it also forms
+ * delta_i = sum_a dO_ia O_ia of its rows and writes it to `workspace`.  Then one
+ * that holds a key/value tile and streams the query tiles that may see it
+ * (dK, dV), reading delta.  Each recomputes its score blocks from q, k and
  * lse: p_ij = e^{s_ij - LSE_i}, gamma_ij = p_ij (dO_i . V_j - delta_i),
  * dQ_i = c sum_j gamma_ij K_j, dK_j = c sum_i gamma_ij Q_i, dV_j = sum_i p_ij dO_i.
  *
@@ -123,10 +124,11 @@ EIAT_API eiat_status attn_bwd(const void *q, const void *k, const void *v, const
 /*
  * One step of the reverse procedure, for callers that schedule or time the
  * steps separately: stage 0 computes delta_i = sum_a dO_ia O_ia into
- * `workspace`; stage 1 computes dK and dV; stage 2 computes dQ.  Stages 1 and 2
- * read delta from `workspace`, so stage 0 must have run on the same workspace
- * (in stream order) first.  attn_bwd is stages 0, 1, 2 in that order.  Outputs
- * a stage does not write are not read and may hold anything.  Arguments,
+ * `workspace`; stage 1 computes dK and dV; stage 2 computes dQ and writes the
+ * same delta into `workspace` (bit for bit what stage 0 writes).  Stage 1 reads
+ * delta from `workspace`, so stage 0 or stage 2 must have run on the same
+ * workspace (in stream order) first.  attn_bwd is stage 2 then stage 1.
+ * Outputs a stage does not write are not read and may hold anything.  Arguments,
  * validation and errors are those of attn_bwd; an unknown stage is
  * EIAT_ERR_INVALID_ARG.
  */

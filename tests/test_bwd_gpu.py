@@ -109,6 +109,33 @@ def test_bwd_train_config_sampled_heads():
     assert float((a - b).abs().max()) <= 0.05 * float(a.abs().max()) + 1.0
 
 
+@pytest.mark.parametrize("dtype,d,n,mask", [("bf16", 64, 300, "causal"), ("f16", 128, 200, "none"),
+                                          ("f32", 16, 129, "causal"), ("bf16", 16, 77, "none"),
+                                          ("f32", 64, 65, "window"), ("f32", 128, 33, "causal")])
+def test_dq_stage_writes_stage0_delta(dtype, d, n, mask):
+    """Stage 2 (dQ) forms the same per-row delta as stage 0, bit for bit, and
+    that delta is sum_a dO_ia O_ia to float32 rounding."""
+    w = Workload("delta", 2, 3, n, d, d, dtype, mask, window=48 if mask == "window" else 0, seed=53)
+    inp, (o, lse), _ = run_fwd_bwd(w)
+    q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
+    nb = attn_bwd_workspace_bytes(2, 3, n)
+    ws0 = torch.full((nb,), 0xFF, dtype=torch.uint8, device=DEV)
+    ws2 = torch.full((nb,), 0xFF, dtype=torch.uint8, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    announce(f"attn_bwd_stage 0 and 2 delta {w}")
+    attn_bwd(q, k, v, o, lse, do, scale=w.c, mask=w.mask, window=w.window, dq=dq, dk=dk, dv=dv,
+             workspace=ws0, stage=0)
+    attn_bwd(q, k, v, o, lse, do, scale=w.c, mask=w.mask, window=w.window, dq=dq, dk=dk, dv=dv,
+             workspace=ws2, stage=2)
+    torch.cuda.synchronize()
+    d0, d2 = ws0.view(torch.int32).cpu(), ws2.view(torch.int32).cpu()
+    assert torch.equal(d0, d2)
+    prod = to64(o) * to64(do)
+    ref = prod.sum(axis=-1).reshape(-1)
+    bound = 1e-5 * np.abs(prod).sum(axis=-1).reshape(-1) + 1e-30
+    assert np.all(np.abs(to64(d0.view(torch.float32)) - ref) <= bound)
+
+
 def test_bwd_stages_equal_full_call():
     """attn_bwd_stage 0, 1, 2 in order gives bitwise the outputs of attn_bwd."""
     w = Workload("stages", 1, 2, 300, 64, 64, "bf16", "causal", seed=47)
