@@ -459,7 +459,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log(f"bench.py: --gpus {args.gpus} (WORLD_SIZE {world}) requested, but this build runs "
+        log(f"bench.py: --gpus {args.gpus} (WORLD_SIZE {world}) requested, but this benchmark runs "
             "on exactly one GPU: the attention path has no multi-GPU code. Run with --gpus 1.")
         sys.exit(2)
 
