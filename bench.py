@@ -39,8 +39,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 PEAK_FP8_FWD = 1.0 / (0.5 / PEAK_TFLOPS["fp8"] + 0.5 / PEAK_TFLOPS["bf16"])
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip",
-                  "attn_fp8.hip"]
+KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip",
+                  "attn_decode.hip", "attn_fp8.hip"]
 DECODE_METRIC = ("decode attention GB/s: algorithmic HBM bytes (Q, K, V read once, O and LSE "
                  "written once) per second")
 

@@ -16,11 +16,14 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libeiat_attn.so")
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fp8.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_decode.hip",
+           "attn_fp8.hip"]
 # Machine-scheduler strategy per source, chosen by timing each kernel file's
 # kernels under the strategies LLVM offers for AMDGPU: max-ilp for the forward
-# (its exp/MFMA interleave) and for the backward (dK/dV 1-4 % faster than under
-# max-memory-clause, dQ within 3 %).
+# (its exp/MFMA interleave) and for delta and dK/dV (1-4 % faster than under
+# max-memory-clause).  The dQ kernel, compiled in its own unit, keeps LLVM's
+# default strategy: 5-10 % faster than under max-ilp at d = 64 causal, within
+# 1 % elsewhere.
 PER_SOURCE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],

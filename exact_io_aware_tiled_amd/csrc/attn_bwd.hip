@@ -134,6 +134,11 @@ __device__ inline float unit_dot(const u32x4& a, const u32x4& b) {
   return acc;
 }
 
+// The dQ kernel is compiled in a unit of its own (attn_bwd_dq.hip defines
+// EIAT_BWD_DQ_UNIT and includes this file), so that it can take another
+// machine-scheduler strategy than the delta and dK/dV kernels.
+#ifndef EIAT_BWD_DQ_UNIT
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const T* __restrict__ O,
                                                              const T* __restrict__ dO,
@@ -523,6 +528,74 @@ __global__ void __launch_bounds__(256)
 }
 
 // ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+template <typename T, int D, int MASK, bool DROP>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  const int64_t rows = a.bh * a.n;
+  if (a.stages & 1) {
+    constexpr int CPR = D * Elt<T>::kBytes / 16;
+    const int64_t blocks = (rows * CPR + 255) / 256;
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dout),
+                       a.delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dQ (which also writes delta) runs before dK/dV, which reads it
+  if (a.stages & 4) {
+    hipError_t e = launch_bwd_dq(a);  // dQ unit
+    if (e != hipSuccess) return e;
+  }
+  if (a.stages & 2) {
+    using C = DkvCfg<T, D>;
+    const int num_ktiles = (int)((a.n + C::BNK - 1) / C::BNK);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, MASK, DROP>),
+                       dim3((unsigned)(num_ktiles * a.bh)), dim3(C::kThreads), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
+                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), (int)a.n, (int)a.bh,
+                       num_ktiles, (int)a.window, a.qk_scale, a.qmode, a.scale, a.drop);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int D, int MASK>
+static hipError_t launch_bwd_m(const BwdArgs& a) {
+  return a.drop.thr > 0 ? launch_bwd_t<T, D, MASK, true>(a) : launch_bwd_t<T, D, MASK, false>(a);
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_d(const BwdArgs& a) {
+  switch (a.mask) {
+    case 0: return launch_bwd_m<T, D, 0>(a);
+    case 1: return launch_bwd_m<T, D, 1>(a);
+    default: return launch_bwd_m<T, D, 2>(a);
+  }
+}
+
+template <typename T>
+static hipError_t launch_bwd_dt(const BwdArgs& a) {
+  switch (a.d) {
+    case 16: return launch_bwd_d<T, 16>(a);
+    case 64: return launch_bwd_d<T, 64>(a);
+    default: return launch_bwd_d<T, 128>(a);
+  }
+}
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  switch (a.dtype) {
+    case 0: return launch_bwd_dt<float>(a);
+    case 1: return launch_bwd_dt<_Float16>(a);
+    default: return launch_bwd_dt<__bf16>(a);
+  }
+}
+
+#else  // EIAT_BWD_DQ_UNIT
+
+// ---------------------------------------------------------------------------
 // 3. dQ: queries resident, key/value tiles streamed
 // ---------------------------------------------------------------------------
 template <typename T, int D>
@@ -758,78 +831,53 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// launch
+// dQ launch
 // ---------------------------------------------------------------------------
 template <typename T, int D, int MASK, bool DROP>
-static hipError_t launch_bwd_t(const BwdArgs& a) {
-  const int64_t rows = a.bh * a.n;
-  if (a.stages & 1) {
-    constexpr int CPR = D * Elt<T>::kBytes / 16;
-    const int64_t blocks = (rows * CPR + 255) / 256;
-    hipLaunchKernelGGL((attn_bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
-                       a.stream, static_cast<const T*>(a.o), static_cast<const T*>(a.dout),
-                       a.delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // dQ (which also writes delta) runs before dK/dV, which reads it
-  if (a.stages & 4) {
-    using C = DqCfg<T, D>;
-    const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK, DROP>),
-                       dim3((unsigned)(num_qtiles * a.bh)), dim3(C::kThreads), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
-                       static_cast<const T*>(a.o), a.lse, a.delta, static_cast<T*>(a.dq),
-                       (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
-                       a.scale, a.drop);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.stages & 2) {
-    using C = DkvCfg<T, D>;
-    const int num_ktiles = (int)((a.n + C::BNK - 1) / C::BNK);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, MASK, DROP>),
-                       dim3((unsigned)(num_ktiles * a.bh)), dim3(C::kThreads), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse, a.delta,
-                       static_cast<T*>(a.dk), static_cast<T*>(a.dv), (int)a.n, (int)a.bh,
-                       num_ktiles, (int)a.window, a.qk_scale, a.qmode, a.scale, a.drop);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+static hipError_t launch_dq_t(const BwdArgs& a) {
+  using C = DqCfg<T, D>;
+  const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK, DROP>),
+                     dim3((unsigned)(num_qtiles * a.bh)), dim3(C::kThreads), 0, a.stream,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
+                     static_cast<const T*>(a.o), a.lse, a.delta, static_cast<T*>(a.dq),
+                     (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
+                     a.scale, a.drop);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int MASK>
-static hipError_t launch_bwd_m(const BwdArgs& a) {
-  return a.drop.thr > 0 ? launch_bwd_t<T, D, MASK, true>(a) : launch_bwd_t<T, D, MASK, false>(a);
+static hipError_t launch_dq_m(const BwdArgs& a) {
+  return a.drop.thr > 0 ? launch_dq_t<T, D, MASK, true>(a) : launch_dq_t<T, D, MASK, false>(a);
 }
 
 template <typename T, int D>
-static hipError_t launch_bwd_d(const BwdArgs& a) {
+static hipError_t launch_dq_d(const BwdArgs& a) {
   switch (a.mask) {
-    case 0: return launch_bwd_m<T, D, 0>(a);
-    case 1: return launch_bwd_m<T, D, 1>(a);
-    default: return launch_bwd_m<T, D, 2>(a);
+    case 0: return launch_dq_m<T, D, 0>(a);
+    case 1: return launch_dq_m<T, D, 1>(a);
+    default: return launch_dq_m<T, D, 2>(a);
   }
 }
 
 template <typename T>
-static hipError_t launch_bwd_dt(const BwdArgs& a) {
+static hipError_t launch_dq_dt(const BwdArgs& a) {
   switch (a.d) {
-    case 16: return launch_bwd_d<T, 16>(a);
-    case 64: return launch_bwd_d<T, 64>(a);
-    default: return launch_bwd_d<T, 128>(a);
+    case 16: return launch_dq_d<T, 16>(a);
+    case 64: return launch_dq_d<T, 64>(a);
+    default: return launch_dq_d<T, 128>(a);
   }
 }
 
-hipError_t launch_bwd(const BwdArgs& a) {
+hipError_t launch_bwd_dq(const BwdArgs& a) {
   switch (a.dtype) {
-    case 0: return launch_bwd_dt<float>(a);
-    case 1: return launch_bwd_dt<_Float16>(a);
-    default: return launch_bwd_dt<__bf16>(a);
+    case 0: return launch_dq_dt<float>(a);
+    case 1: return launch_dq_dt<_Float16>(a);
+    default: return launch_dq_dt<__bf16>(a);
   }
 }
+
+#endif  // EIAT_BWD_DQ_UNIT
 
 }  // namespace eiat

@@ -118,5 +118,7 @@ hipError_t launch_quant_fp8(const QuantArgs& a);
 hipError_t launch_quant_fp8_v(const QuantVArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
+// The dQ kernel alone (stage bit 2); launch_bwd calls it.
+hipError_t launch_bwd_dq(const BwdArgs& a);
 
 }  // namespace eiat
