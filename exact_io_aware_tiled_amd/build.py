@@ -22,8 +22,8 @@ SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "a
 # kernels under the strategies LLVM offers for AMDGPU: max-ilp for the forward
 # (its exp/MFMA interleave) and for delta and dK/dV (1-4 % faster than under
 # max-memory-clause).  The dQ kernel, compiled in its own unit, keeps LLVM's
-# default strategy: 5-10 % faster than under max-ilp at d = 64 causal, within
-# 1 % elsewhere.
+# default strategy: 1-5 % faster than under max-ilp at n = 4096 causal (d = 64
+# and 128), 1 % slower at d = 128 without mask, n = 16384.
 PER_SOURCE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
