@@ -108,17 +108,60 @@ def _stream_handle(stream: Optional[torch.cuda.Stream]):
 
 
 def _dims(q: torch.Tensor, v: torch.Tensor):
-    if q.dim() != 4 or v.dim() != 4:
+    if not isinstance(q, torch.Tensor) or not isinstance(v, torch.Tensor) or q.dim() != 4 \
+            or v.dim() != 4:
         raise ValueError("expected [B, H, n, d] tensors")
     B, H, n, d = q.shape
     return B, H, n, d, v.shape[-1]
 
 
-def _require(t: torch.Tensor, name: str):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _validate(specs):
+    """Check every tensor a call hands to the library, outputs included, before
+    any launch: ``specs`` is a list of (name, tensor, shape, dtype), where shape
+    is a tuple (or None to skip) and dtype a torch dtype, a tuple of allowed
+    dtypes, or None.  Shapes and dtypes are checked first, then contiguity,
+    then that every tensor sits on the same GPU; the first mismatch raises
+    ValueError.  The C ABI receives raw pointers and the sizes derived from
+    the inputs, so a short or mistyped buffer here would otherwise become
+    out-of-bounds device accesses."""
+    for name, t, shape, dtype in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtype is not None:
+            allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+            if t.dtype not in allowed:
+                raise ValueError(f"{name} has dtype {t.dtype}, expected "
+                                 + " or ".join(str(a) for a in allowed))
+    for name, t, _, _ in specs:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dev = None
+    for name, t, _, _ in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+FLOAT_TYPES = tuple(DTYPE_CODES)
+HALF_TYPES = (torch.float16, torch.bfloat16)
+
+
+def _float_dtype(t: torch.Tensor, name: str, allowed=FLOAT_TYPES):
+    if t.dtype not in allowed:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected "
+                         + " or ".join(str(a) for a in allowed))
+    return t.dtype
+
+
+def _workspace(ws, name="workspace"):
+    if not isinstance(ws, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    return (name, ws, None, None)
 
 
 def attn_fwd(q, k, v, scale: Optional[float] = None, mask: str = "causal", window: int = 0,
@@ -127,15 +170,16 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, mask: str = "causal", windo
 
     p_drop > 0 applies dropout to the weights (attn_fwd_dropout; mask keyed on seed)."""
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name)
     B, H, n, d, dv = _dims(q, v)
+    dt = _float_dtype(q, "q")
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty(B, H, n, dv, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+    _validate([("q", q, (B, H, n, d), dt), ("k", k, (B, H, n, d), dt), ("v", v, (B, H, n, dv), dt),
+               ("out", out, (B, H, n, dv), dt), ("lse", lse, (B, H, n), torch.float32)])
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n, d,
             dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask], int(window))
     if p_drop:
@@ -150,17 +194,20 @@ def attn_quant_fp8(x, signs=None, codes=None, scales=None, stream=None):
     [..., d] and E8M0 scale bytes [..., d / 32]; ``signs`` (int8 [d] of +-1 on
     the GPU) rotates the rows as H (signs * x) first."""
     lib = load_library()
-    _require(x, "x")
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise ValueError("x must be a tensor of rows [..., d]")
+    _float_dtype(x, "x")
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
     if codes is None:
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+    specs = [("x", x, None, None), ("codes", codes, tuple(x.shape), torch.uint8),
+             ("scales", scales, tuple(x.shape[:-1]) + (d // 32,), torch.uint8)]
     if signs is not None:
-        _require(signs, "signs")
-        if signs.dtype != torch.int8 or signs.numel() != d:
-            raise ValueError("signs must be int8 with d entries")
+        specs.append(("signs", signs, (d,), torch.int8))
+    _validate(specs)
     _check(lib.attn_quant_fp8(x.data_ptr(), None if signs is None else signs.data_ptr(),
                               codes.data_ptr(), scales.data_ptr(), rows, d, DTYPE_CODES[x.dtype],
                               _stream_handle(stream)))
@@ -173,16 +220,17 @@ def attn_fwd_fp8(q, q_scale, k, k_scale, v, scale: float, mask: str = "causal", 
     q_scale, k_scale: uint8 [B, H, n, d / 32]; v: [B, H, n, dv] f16/bf16.  ``scale``
     multiplies the dequantized products (c / d for rows rotated by attn_quant_fp8)."""
     lib = load_library()
-    for name, t in (("q", q), ("q_scale", q_scale), ("k", k), ("k_scale", k_scale), ("v", v)):
-        _require(t, name)
-    for name, t in (("q", q), ("q_scale", q_scale), ("k", k), ("k_scale", k_scale)):
-        if t.dtype != torch.uint8:
-            raise ValueError(f"{name} must be uint8")
     B, H, n, d, dv = _dims(q, v)
+    dt = _float_dtype(v, "v", HALF_TYPES)
+    u8 = torch.uint8
     if out is None:
         out = torch.empty(B, H, n, dv, dtype=v.dtype, device=v.device)
     if lse is None:
         lse = torch.empty(B, H, n, dtype=torch.float32, device=v.device)
+    _validate([("q", q, (B, H, n, d), u8), ("q_scale", q_scale, (B, H, n, d // 32), u8),
+               ("k", k, (B, H, n, d), u8), ("k_scale", k_scale, (B, H, n, d // 32), u8),
+               ("v", v, (B, H, n, dv), dt), ("out", out, (B, H, n, dv), dt),
+               ("lse", lse, (B, H, n), torch.float32)])
     _check(lib.attn_fwd_fp8(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
                             v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n, d, dv,
                             DTYPE_CODES[v.dtype], float(scale), MASK_CODES[mask], int(window),
@@ -195,15 +243,17 @@ def attn_quant_fp8_v(v, codes=None, scales=None, stream=None):
     (attn_quant_fp8_v): uint8 [B, H, nt, dv, 64] and [B, H, nt, dv, 2], nt =
     ceil(n / 64), in the tile-major key order the FP8 value product reads."""
     lib = load_library()
-    _require(v, "v")
-    if v.dim() != 4:
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
         raise ValueError("expected v of shape [B, H, n, dv]")
+    _float_dtype(v, "v")
     B, H, n, dv = v.shape
     nt = (n + 63) // 64
     if codes is None:
         codes = torch.empty(B, H, nt, dv, 64, dtype=torch.uint8, device=v.device)
     if scales is None:
         scales = torch.empty(B, H, nt, dv, 2, dtype=torch.uint8, device=v.device)
+    _validate([("v", v, None, None), ("codes", codes, (B, H, nt, dv, 64), torch.uint8),
+               ("scales", scales, (B, H, nt, dv, 2), torch.uint8)])
     _check(lib.attn_quant_fp8_v(v.data_ptr(), codes.data_ptr(), scales.data_ptr(), B * H, n, dv,
                                 DTYPE_CODES[v.dtype], _stream_handle(stream)))
     return codes, scales
@@ -215,19 +265,23 @@ def attn_fwd_fp8_pv(q, q_scale, k, k_scale, v, v_scale, scale: float, mask: str 
     q_scale, k_scale as attn_fwd_fp8; v, v_scale from attn_quant_fp8_v; O in
     ``dtype`` (float16 or bfloat16)."""
     lib = load_library()
-    for name, t in (("q", q), ("q_scale", q_scale), ("k", k), ("k_scale", k_scale), ("v", v),
-                    ("v_scale", v_scale)):
-        _require(t, name)
-        if t.dtype != torch.uint8:
-            raise ValueError(f"{name} must be uint8")
-    if q.dim() != 4 or v.dim() != 5:
+    if (not isinstance(q, torch.Tensor) or not isinstance(v, torch.Tensor) or q.dim() != 4
+            or v.dim() != 5):
         raise ValueError("expected q [B, H, n, d] and v [B, H, nt, dv, 64]")
     B, H, n, d = q.shape
     dv = v.shape[-2]
+    nt = (n + 63) // 64
+    u8 = torch.uint8
     if out is None:
+        if dtype not in HALF_TYPES:
+            raise ValueError(f"dtype {dtype} must be float16 or bfloat16")
         out = torch.empty(B, H, n, dv, dtype=dtype, device=q.device)
     if lse is None:
         lse = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+    _validate([("q", q, (B, H, n, d), u8), ("q_scale", q_scale, (B, H, n, d // 32), u8),
+               ("k", k, (B, H, n, d), u8), ("k_scale", k_scale, (B, H, n, d // 32), u8),
+               ("v", v, (B, H, nt, dv, 64), u8), ("v_scale", v_scale, (B, H, nt, dv, 2), u8),
+               ("out", out, (B, H, n, dv), HALF_TYPES), ("lse", lse, (B, H, n), torch.float32)])
     _check(lib.attn_fwd_fp8_pv(q.data_ptr(), q_scale.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
                                v.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
                                H, n, d, dv, DTYPE_CODES[out.dtype], float(scale), MASK_CODES[mask],
@@ -250,9 +304,9 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "ca
     p_drop > 0 replays the dropout of attn_fwd(..., p_drop, seed) (same values).
     """
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do)):
-        _require(t, name)
     B, H, n, d, dvd = _dims(q, v)
+    dt = _float_dtype(q, "q")
+    qs, vs = (B, H, n, d), (B, H, n, dvd)
     if scale is None:
         scale = d ** -0.5
     dq = torch.empty_like(q) if dq is None else dq
@@ -261,6 +315,9 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "ca
     ws_bytes = attn_bwd_workspace_bytes(B, H, n)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _validate([("q", q, qs, dt), ("k", k, qs, dt), ("v", v, vs, dt), ("o", o, vs, dt),
+               ("lse", lse, (B, H, n), torch.float32), ("do", do, vs, dt),
+               ("dq", dq, qs, dt), ("dk", dk, qs, dt), ("dv", dv, vs, dt), _workspace(workspace)])
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), B, H, n, d, dvd, DTYPE_CODES[q.dtype],
@@ -293,13 +350,12 @@ def attn_decode(q, k, v, scale: Optional[float] = None, mask: str = "none", wind
     summaries into `workspace`; their merge into out, lse) -- pass the same workspace.
     """
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name)
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-d")
+    if any(not isinstance(t, torch.Tensor) or t.dim() != 4 for t in (q, k, v)):
+        raise ValueError("q, k, v must be 4-d tensors")
     B, H, nq, d = q.shape
     Hkv, nk = k.shape[1], k.shape[2]
     dv = v.shape[-1]
+    dt = _float_dtype(q, "q")
     if scale is None:
         scale = d ** -0.5
     if out is None:
@@ -309,6 +365,9 @@ def attn_decode(q, k, v, scale: Optional[float] = None, mask: str = "none", wind
     ws_bytes = attn_decode_workspace_bytes(B, H, Hkv, nq, nk, dv)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _validate([("q", q, (B, H, nq, d), dt), ("k", k, (B, Hkv, nk, d), dt),
+               ("v", v, (B, Hkv, nk, dv), dt), ("out", out, (B, H, nq, dv), dt),
+               ("lse", lse, (B, H, nq), torch.float32), _workspace(workspace)])
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, Hkv, nq, nk,
             d, dv, DTYPE_CODES[q.dtype], float(scale), MASK_CODES[mask], int(window),
