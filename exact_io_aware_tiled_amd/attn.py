@@ -59,6 +59,9 @@ def load_library():
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                              i64, i64, i64, c_int, c_float, c_int, i64, vp]
     lib.attn_bwd.restype = c_int
+    lib.attn_bwd_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, c_int, c_float, c_int,
+                                                i64, vp]
+    lib.attn_bwd_noalloc.restype = c_int
     lib.attn_bwd_stage.argtypes = [c_int] + lib.attn_bwd.argtypes
     lib.attn_bwd_stage.restype = c_int
     lib.attn_fwd_dropout.argtypes = lib.attn_fwd.argtypes[:-1] + [c_float, ctypes.c_uint64, vp]
@@ -333,6 +336,28 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, mask: str = "ca
         _check(lib.attn_bwd(*args, sh))
     else:
         _check(lib.attn_bwd_stage(int(stage), *args, sh))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale: Optional[float] = None,
+                     mask: str = "causal", window: int = 0, stream=None):
+    """attn_bwd_noalloc: dQ, dK, dV into the caller's dq, dk, dv, with the
+    per-row delta in the library's own per-GPU scratch (no workspace, nothing
+    allocated by this call; B * H * n up to 4,194,304 rows).  Calls that
+    overlap on one GPU race on that scratch."""
+    lib = load_library()
+    B, H, n, d, dvd = _dims(q, v)
+    dt = _float_dtype(q, "q")
+    qs, vs = (B, H, n, d), (B, H, n, dvd)
+    _validate([("q", q, qs, dt), ("k", k, qs, dt), ("v", v, vs, dt), ("o", o, vs, dt),
+               ("lse", lse, (B, H, n), torch.float32), ("do", do, vs, dt),
+               ("dq", dq, qs, dt), ("dk", dk, qs, dt), ("dv", dv, vs, dt)])
+    if scale is None:
+        scale = d ** -0.5
+    _check(lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), B, H, n, d, dvd, DTYPE_CODES[q.dtype], float(scale),
+                                MASK_CODES[mask], int(window), _stream_handle(stream)))
     return dq, dk, dv
 
 

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/eiat_attn.h"
 #include "attn_internal.h"
 
@@ -318,12 +320,56 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n) {
   return (size_t)B * (size_t)H * (size_t)n * sizeof(float);
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of attn_bwd_noalloc: the per-row delta of the backward, in a
+// file-scope device array instead of a caller-passed workspace.  Each GPU the
+// library runs on holds its own copy (16 MiB) until the process ends; host
+// code only ever uses the per-device address from hipGetSymbolAddress (the
+// array's name in host code is a stand-in, not a device address).  Every call
+// on a GPU shares that GPU's copy, so calls that overlap on one GPU (several
+// streams, several host threads) race on it.  Nothing in it needs to start at
+// zero: the dQ kernel writes the delta of every row before the dK/dV kernel
+// reads it, in stream order.
+// ---------------------------------------------------------------------------
+constexpr int64_t kNoAllocMaxRows = int64_t(1) << 22;  // B * H * n limit (4,194,304 rows)
+static __device__ __align__(256) float scratch[kNoAllocMaxRows];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current (the entry point's first call on it).  Null on a HIP error.
+float* scratch_for_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+// The backward's entry points.  scratch_ws: delta goes to this GPU's copy of
+// `scratch` (attn_bwd_noalloc); workspace and workspace_bytes are then unused.
 static eiat_status bwd_impl(int stages, const void* q, const void* k, const void* v,
                             const void* o, const void* dout, const float* lse, void* dq, void* dk,
                             void* dvv, void* workspace, size_t workspace_bytes, int64_t B,
                             int64_t H, int64_t n, int64_t d, int64_t dv, int dtype, float scale,
                             int mask, int64_t window, const eiat::DropParams& drop,
-                            void* stream) {
+                            void* stream, bool scratch_ws = false) {
   bool empty = false;
   float qk_scale = 1.0f;
   int qmode = 0;
@@ -332,12 +378,16 @@ static eiat_status bwd_impl(int stages, const void* q, const void* k, const void
       check_common(B, H, n, d, dv, dtype, scale, mask, window, &empty, &qk_scale, &qmode, &win);
   if (s != EIAT_OK) return s;
   if (empty) return ok();
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dvv || !workspace)
+  if (scratch_ws && B * H * n > kNoAllocMaxRows)
+    return fail(EIAT_ERR_UNSUPPORTED,
+                "B * H * n = %lld rows exceed the %lld rows of the no-allocation scratch; use "
+                "attn_bwd with a workspace", (long long)(B * H * n), (long long)kNoAllocMaxRows);
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dvv || (!scratch_ws && !workspace))
     return fail(EIAT_ERR_INVALID_ARG, "null pointer argument");
-  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dvv, workspace};
+  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dvv, scratch_ws ? q : workspace};
   for (int i = 0; i < 10; ++i)
     if (!aligned16(ptrs[i])) return fail(EIAT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  if (workspace_bytes < attn_bwd_workspace_bytes(B, H, n))
+  if (!scratch_ws && workspace_bytes < attn_bwd_workspace_bytes(B, H, n))
     return fail(EIAT_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
                 attn_bwd_workspace_bytes(B, H, n));
   const size_t eb = elem_bytes(dtype);
@@ -346,7 +396,7 @@ static eiat_status bwd_impl(int stages, const void* q, const void* k, const void
   const void* ins[6] = {q, k, v, o, dout, lse};
   const size_t insz[6] = {qb, qb, vb, vb, vb, lb};
   void* outs[4] = {dq, dk, dvv, workspace};
-  const size_t outsz[4] = {qb, qb, vb, attn_bwd_workspace_bytes(B, H, n)};
+  const size_t outsz[4] = {qb, qb, vb, scratch_ws ? 0 : attn_bwd_workspace_bytes(B, H, n)};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
@@ -354,6 +404,12 @@ static eiat_status bwd_impl(int stages, const void* q, const void* k, const void
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
         return fail(EIAT_ERR_INVALID_ARG, "outputs must not overlap each other");
+  }
+  if (scratch_ws) {
+    hipError_t e = hipSuccess;
+    workspace = scratch_for_current_device(&e);
+    if (!workspace)
+      return fail(EIAT_ERR_HIP, "no-allocation scratch address: %s", hipGetErrorString(e));
   }
 
   eiat::BwdArgs a;
@@ -416,6 +472,14 @@ eiat_status attn_bwd_dropout_stage(int stage, const void* q, const void* k, cons
   if (s != EIAT_OK) return s;
   return bwd_impl(1 << stage, q, k, v, o, dout, lse, dq, dk, dvv, workspace, workspace_bytes, B, H,
                   n, d, dv, dtype, scale, mask, window, dp, stream);
+}
+
+eiat_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dvv,
+                             int64_t B, int64_t H, int64_t n, int64_t d, int64_t dv, int dtype,
+                             float scale, int mask, int64_t window, void* stream) {
+  return bwd_impl(6, q, k, v, o, dout, lse, dq, dk, dvv, nullptr, 0, B, H, n, d, dv, dtype, scale,
+                  mask, window, kNoDrop, stream, true);
 }
 
 eiat_status attn_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,

@@ -52,9 +52,10 @@
 extern "C" {
 #endif
 
-#define EIAT_ABI_VERSION 5  /* 2: adds attn_decode; 3: adds the dropout entry points;
+#define EIAT_ABI_VERSION 6  /* 2: adds attn_decode; 3: adds the dropout entry points;
                                4: adds attn_quant_fp8 and attn_fwd_fp8;
-                               5: adds attn_quant_fp8_v and attn_fwd_fp8_pv */
+                               5: adds attn_quant_fp8_v and attn_fwd_fp8_pv;
+                               6: adds attn_bwd_noalloc */
 
 /* Symbols of the shared library (built with hidden default visibility). */
 #if defined(__GNUC__)
@@ -139,7 +140,30 @@ EIAT_API eiat_status attn_bwd_stage(int stage, const void *q, const void *k, con
                                     int dtype, float scale, int mask, int64_t window,
                                     void *stream);
 
-/* Static string naming a status code. */
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory around the call (code under stream or graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The per-row delta lives
+ * instead in a fixed device array inside the library, one per GPU (16 MiB,
+ * held from the first call on that GPU until the process ends), so the call
+ * itself allocates nothing: it computes exactly what attn_bwd computes (same
+ * kernels, bitwise the same dq, dk, dvv).
+ *   Limit: B * H * n <= 4,194,304 rows; larger problems return
+ *          EIAT_ERR_UNSUPPORTED (use attn_bwd with a workspace).
+ *   Sharing: every call on a GPU uses that GPU's array, which keeps the last
+ *          call's contents.  Calls that overlap in time on one GPU (different
+ *          streams or host threads) race on it and must be serialized by the
+ *          caller; calls on one stream are ordered by the stream.
+ * Arguments, layout, validation and other errors as attn_bwd (workspace and
+ * workspace_bytes are absent); a failure to look up the array's device
+ * address is EIAT_ERR_HIP.
+ */
+EIAT_API eiat_status attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                                      const void *dout, const float *lse, void *dq, void *dk,
+                                      void *dvv, int64_t B, int64_t H, int64_t n, int64_t d,
+                                      int64_t dv, int dtype, float scale, int mask,
+                                      int64_t window, void *stream);
+
 /*
  * Forward and reverse with dropout on the attention weights.  The pages fix
  * only the requirement (alphabetamath.cc, Algorithm "Exact tiled softmax
@@ -299,6 +323,7 @@ EIAT_API eiat_status attn_fwd_fp8_pv(const uint8_t *q, const uint8_t *q_scale, c
                                      int64_t H, int64_t n, int64_t d, int64_t dv, int dtype,
                                      float scale, int mask, int64_t window, void *stream);
 
+/* Static string naming a status code. */
 EIAT_API const char *attn_status_string(int status);
 
 /* Thread-local detail of the calling thread's last non-OK return ("" if none). */

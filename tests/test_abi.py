@@ -17,6 +17,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = A.header_functions()
     assert set(names) == {"attn_fwd", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
+                          "attn_bwd_noalloc",
                           "attn_fwd_dropout", "attn_bwd_dropout", "attn_bwd_dropout_stage",
                           "attn_decode", "attn_decode_stage", "attn_decode_workspace_bytes",
                           "attn_quant_fp8", "attn_fwd_fp8", "attn_quant_fp8_v", "attn_fwd_fp8_pv",
@@ -24,7 +25,7 @@ def test_exports_every_declared_function(lib):
                           "attn_last_error", "attn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -260,3 +261,32 @@ def fwd8pv(lib, q=F, qs=F * 2**20, k=F * 2**21, ks=F * 2**22, v=F * 2**23, vs=F 
 def test_fwd_fp8_pv_rejects(lib, kw, code):
     assert fwd8pv(lib, **kw) == code
     assert lib.attn_last_error() != b""
+
+
+def bwd_noalloc(lib, **kw):
+    args = dict(q=F, k=F * 2**20, v=F * 2**21, o=F * 2**22, do=F * 2**23, lse=F * 2**24,
+                dq=F * 2**25, dk=F * 2**26, dv=F * 2**27, B=1, H=1, n=64, d=64, dv_=64, dtype=2,
+                scale=0.125, mask=1, window=0)
+    args.update(kw)
+    return lib.attn_bwd_noalloc(args["q"], args["k"], args["v"], args["o"], args["do"],
+                                args["lse"], args["dq"], args["dk"], args["dv"], args["B"],
+                                args["H"], args["n"], args["d"], args["dv_"], args["dtype"],
+                                args["scale"], args["mask"], args["window"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(dk=0), 1), (dict(B=-1), 1), (dict(mask=2, window=0), 1),
+    (dict(dq=F), 1),  # output overlaps q
+    (dict(d=32, dv_=32), 2),
+    # beyond the scratch: B * H * n > 4,194,304 rows, rejected before any HIP call
+    (dict(B=2, H=32, n=65537), 2), (dict(B=1, H=1, n=(1 << 22) + 1), 2),
+])
+def test_bwd_noalloc_rejects(lib, kw, code):
+    assert bwd_noalloc(lib, **kw) == code
+    assert lib.attn_last_error() != b""
+
+
+def test_bwd_noalloc_limit_message_and_empty(lib):
+    assert bwd_noalloc(lib, B=4, H=16, n=65536 + 1) == 2
+    assert b"no-allocation scratch" in lib.attn_last_error()
+    assert bwd_noalloc(lib, n=0, q=0, k=0) == 0  # nothing to do, no GPU touched
