@@ -39,8 +39,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 PEAK_FP8_FWD = 1.0 / (0.5 / PEAK_TFLOPS["fp8"] + 0.5 / PEAK_TFLOPS["bf16"])
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["attn_device.h", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip",
-                  "attn_decode.hip", "attn_fp8.hip"]
+KERNEL_SOURCES = ["attn_device.h", "attn_internal.h", "attn_bwd_common.h", "attn_fwd.hip",
+                  "attn_bwd.hip", "attn_bwd_dq.hip", "attn_decode.hip", "attn_fp8.hip"]
 DECODE_METRIC = ("decode attention GB/s: algorithmic HBM bytes (Q, K, V read once, O and LSE "
                  "written once) per second")
 
@@ -67,12 +67,15 @@ def convention_pairs(n: int, mask: str, window: int) -> float:
 
 
 def sources_digest() -> str:
-    """Hash of the kernel sources with comments removed, and of the per-source
-    compile flags: a change to the code or to how it is compiled invalidates the
-    committed counter summaries, a change to a comment does not."""
+    """Hash of the kernel sources with comments removed, of the compile flags
+    (common and per source) and of the target architecture: a change to the
+    code or to how it is compiled invalidates the committed counter summaries,
+    a change to a comment does not."""
     from exact_io_aware_tiled_amd import build as _build
     h = hashlib.sha256()
     h.update(repr(sorted(_build.PER_SOURCE_FLAGS.items())).encode())
+    h.update(repr([f for f in _build.CFLAGS if not f.startswith("-I")]).encode())
+    h.update(_build.ARCH.encode())
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "exact_io_aware_tiled_amd", "csrc", name)) as f:
             text = f.read()
@@ -107,6 +110,39 @@ def load_activity(kernel: str, workload) -> dict | None:
     entry = _counter_entry(kernel, workload)
     act = entry.get("activity") if entry else None
     return {"kernel": kernel, **act, "source": "profiles/attn_activity_counters.txt"} if act else None
+
+
+def device_info(torch, kernel: str | None = None, workload=None) -> dict:
+    """The GPU the run sees: compute units and peak engine clock reported by the
+    HIP runtime, the dense 16-bit MFMA peak they imply (CUs x 4096 FLOP/clk x
+    clock), and, when the committed counter summary of `kernel` on this
+    workload is current, the engine clock observed under that kernel (its
+    GRBM_GUI_ACTIVE cycles over its traced duration) with the peak at that clock.
+    The roofline fraction itself stays against the published peak."""
+    import ctypes
+
+    dev = torch.cuda.current_device()
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "cus": props.multi_processor_count, "max_sclk_mhz": None}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, dev) == 0:  # hipDeviceAttributeClockRate (kHz)
+            info["max_sclk_mhz"] = round(val.value / 1000.0, 1)
+    except OSError:
+        pass
+    if info["max_sclk_mhz"]:
+        info["mfma16_peak_at_max_sclk_tflops"] = round(
+            info["cus"] * 4096 * info["max_sclk_mhz"] * 1e6 / 1e12, 1)
+    entry = _counter_entry(kernel, workload) if kernel else None
+    act = entry.get("activity") if entry else None
+    if act and act.get("sclk_mhz"):
+        info["observed_sclk_mhz"] = act["sclk_mhz"]
+        info["mfma16_peak_at_observed_sclk_tflops"] = round(
+            info["cus"] * 4096 * act["sclk_mhz"] * 1e6 / 1e12, 1)
+        info["observed_sclk_source"] = "profiles/attn_activity_counters.txt"
+    return info
 
 
 def cpu_baseline(w, budget_s: float):
@@ -289,6 +325,7 @@ def bench_fp8(args, w):
         "kernels": per_kernel,
         "roofline": roof,
         "counters": load_activity(dom, w),
+        "device": device_info(torch, dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -429,6 +466,7 @@ def bench_decode(args, w):
         "kernels": per_kernel,
         "roofline": roof,
         "counters": load_activity(dom, w),
+        "device": device_info(torch, dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -598,6 +636,7 @@ def main():
         "kernels": per_kernel,
         "roofline": roof,
         "counters": None if pdrop else load_activity(dom, w),
+        "device": device_info(torch, dom, w),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

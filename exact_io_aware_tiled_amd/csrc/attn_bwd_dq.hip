@@ -1,6 +1,302 @@
-// The dQ kernel of the backward pass (alphabetamath.cc, Algorithm "Exact tiled
-// softmax attention with block-recomputed vector-Jacobian products", reverse
-// procedure), compiled apart from the rest of attn_bwd.hip so that it can take
-// its own machine-scheduler strategy.
-#define EIAT_BWD_DQ_UNIT 1
-#include "attn_bwd.hip"
+// attn_bwd_dq.hip -- the dQ kernel of the backward pass, for gfx950.
+//
+// Follows alphabetamath.cc, "Exact tiled attention and memory-aware
+// differentiation", the Algorithm's reverse procedure: with the forward's row
+// statistics frozen (LSE_i = m_i + ln l_i, so p_ij = e^{s_ij - LSE_i}), a
+// workgroup keeps 128 query rows (Q, dO, LSE and delta_i = sum_a dO_ia O_ia,
+// which it forms and writes for the dK/dV kernel) in registers and streams the
+// key/value tiles those rows may see through LDS, recomputing each score
+// block: gamma_ij = p_ij (sum_a G_ia V_ja - delta_i), dQ_i = c sum_j gamma_ij K_j.
+// No atomics: every dQ row is owned by one wave.
+//
+// Compiled in its own translation unit (not with attn_bwd.hip) so that it
+// keeps LLVM's default machine-scheduler strategy.
+#include "attn_bwd_common.h"
+#include "attn_internal.h"
+
+namespace eiat {
+
+// ---------------------------------------------------------------------------
+// 3. dQ: queries resident, key/value tiles streamed
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DqCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BM = 32 * kWaves;
+  static constexpr int S = Elt<T>::kBytes;
+  static constexpr int BN = (S == 4 && D >= 128) ? 32 : 64;  // keys per streamed tile
+  static constexpr int DP = D < 32 ? 32 : D;
+  // 16-bit: the K^T operand comes from the natural K tile through transpose
+  // reads; float32 keeps a transposed copy.
+  static constexpr bool kTr = (S == 2);
+  static constexpr int NROW = (kTr ? DP : D) * S + 16;  // K, V natural rows
+  static constexpr int TROW = BN * S + 16;              // K^T rows (float32)
+  static constexpr int KN = 0;
+  static constexpr int KT = KN + BN * NROW;
+  static constexpr int VN = KT + (kTr ? 0 : DP * TROW);
+  static constexpr int BUF = VN + BN * NROW;
+  static constexpr int NCH = D * S / 32;
+  static constexpr int NOB = DP / 32;
+  static constexpr int NSB = BN / 32;
+  static constexpr bool kDirect = kTr && D >= 32;
+};
+
+template <typename T, int D, int MASK, bool DROP>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const T* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ delta, T* __restrict__ dQ, int n, int bh_count, int num_qtiles,
+    int window, float qk_scale, int qmode, float scale, DropParams dpar) {
+  using C = DqCfg<T, D>;
+  constexpr int BN = C::BN;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+  using StK = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, !C::kTr>;
+  using StV = Stager<T, D, BN, C::kThreads, C::NROW, C::TROW, true, false>;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  const int bh = bid % bh_count;
+  int qt = bid / bh_count;
+  if (MASK != 0) qt = num_qtiles - 1 - qt;
+  const int q0 = qt * C::BM;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + l32;
+
+  const int64_t head = (int64_t)bh * n;
+  const char* Qh = reinterpret_cast<const char*>(Q + head * D);
+  const char* Kh = reinterpret_cast<const char*>(K + head * D);
+  const char* Vh = reinterpret_cast<const char*>(V + head * D);
+  const char* dOh = reinterpret_cast<const char*>(dO + head * D);
+
+  u32x4 qf[C::NCH], of[C::NCH];
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    qf[c] = qrow < n ? ldg16(Qh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
+    of[c] = qrow < n ? ldg16(dOh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
+    if (qmode == 1) qf[c] ^= Elt<T>::kSign;
+    if (qmode == 2) qf[c] = zero4();  // c = 0: every score is exactly 0
+  }
+  const float lse2 = qrow < n ? LSE[head + qrow] * kLog2e : INFINITY;
+  // delta of this row from its O and the dO chunks above (unit 2c + h of the
+  // row is chunk c of half h), summed in unit_dot's tree; written out for the
+  // dK/dV kernel.
+  float dlt;
+  {
+    const char* Oh = reinterpret_cast<const char*>(O + head * D);
+    float u[C::NCH];
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c)
+      u[c] = unit_dot<T>(qrow < n ? ldg16(Oh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4(),
+                         of[c]);
+#pragma unroll
+    for (int off = C::NCH / 2; off > 0; off >>= 1)
+#pragma unroll
+      for (int c = 0; c < off; ++c) u[c] += u[c + off];
+    dlt = u[0] + __shfl_xor(u[0], 32, 64);
+    if (qrow >= n) dlt = 0.0f;
+    else if (h == 0) delta[head + qrow] = dlt;
+  }
+  // Dropout (DROP): this row's key of the realized mask.
+  const uint32_t row_key = DROP ? drop_row_key(dpar, (uint32_t)bh, (uint32_t)qrow) : 0u;
+
+  int kend = n;
+  if (MASK != 0) kend = min(n, q0 + C::BM);
+  int kbeg = 0;
+  if (MASK == 2) kbeg = max(0, q0 - window + 1);
+  const int t_lo = kbeg / BN, t_hi = (kend + BN - 1) / BN;
+
+  f32x16 dq[C::NOB];
+#pragma unroll
+  for (int ob = 0; ob < C::NOB; ++ob)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[ob][e] = 0.0f;
+
+  for (int b = 0; b < 2; ++b) {
+    if constexpr (C::kTr)
+      zero_pad_cols<D, C::DP, C::S, BN, C::NROW, C::kThreads>(smem + b * C::BUF + C::KN, tid);
+    else
+      zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + b * C::BUF + C::KT, tid);
+  }
+
+  TileLoader<BN, D * C::S / 16, C::kWaves> tl;
+  if constexpr (C::kDirect) tl.init(wave, lane);
+  StK sk;
+  StV sv;
+  auto load_tile = [&](int t) {
+    if constexpr (C::kDirect) {
+      char* b = smem + ((t - t_lo) & 1) * C::BUF;
+      tl.load(b + C::KN, Kh, t * BN, n, wave, lane);
+      tl.load(b + C::VN, Vh, t * BN, n, wave, lane);
+    } else {
+      sk.load(Kh, t * BN, n, tid);
+      sv.load(Vh, t * BN, n, tid);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if constexpr (C::kDirect) {
+      wait_tile_loads();
+    } else {
+      char* b = smem + buf * C::BUF;
+      sk.store(b + C::KN, b + C::KT, tid);
+      sv.store(b + C::VN, nullptr, tid);
+    }
+  };
+
+  load_tile(t_lo);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    const bool has_next = t + 1 < t_hi;
+    if (has_next) load_tile(t + 1);
+    const int j0 = t * BN;
+    bool empty = false;
+    if (MASK != 0) empty = j0 > qw0 + 31;
+    if (MASK == 2) empty = empty || (j0 + BN - 1 < qw0 - window + 1);
+    if (!empty) {
+      const char* b = smem + buf * C::BUF;
+      bool straddle = j0 + BN > n;
+      if (MASK != 0) straddle = straddle || (j0 + BN - 1 > qw0);
+      if (MASK == 2) straddle = straddle || (j0 < qw0 + 31 - window + 1);
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        // scheduling hint: interleave LDS operand reads with the MFMAs
+        __builtin_amdgcn_iglp_opt(0);
+        // S^T = K Q^T and dP^T = V dO^T: lane holds one query row, 16 keys per half
+        // (without dropout dP^T starts at -delta of the lane's row, so
+        // dS = p (dP - delta) needs no subtraction afterwards)
+        f32x16 s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[e] = 0.0f;
+          dp[e] = DROP ? 0.0f : -dlt;
+        }
+        const int rk = 32 * sb + l32;
+#pragma unroll
+        for (int c = 0; c < C::NCH; ++c) {
+          u32x4 ka = *reinterpret_cast<const u32x4*>(b + C::KN + rk * C::NROW + 32 * c + 16 * h);
+          u32x4 va = *reinterpret_cast<const u32x4*>(b + C::VN + rk * C::NROW + 32 * c + 16 * h);
+          s = Elt<T>::mma(ka, qf[c], s);
+          dp = Elt<T>::mma(va, of[c], dp);
+        }
+        if (straddle) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (!key_allowed<MASK>(qrow, j, n, window)) s[e] = -INFINITY;
+          }
+        }
+        if constexpr (DROP) {
+          const int jb = j0 + 32 * sb + 4 * h;  // key of element e = 0
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t bytes = drop_group_bytes(row_key, (uint32_t)(jb + 8 * k) >> 2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int e = 4 * k + r;
+              const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
+              const bool keep = drop_keep(bytes, r, dpar.thr);
+              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) - dlt);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
+            dp[e] = p * dp[e];
+          }
+        }
+        PChunks<T> dsc;
+        dsc.set(dp);
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) {
+#pragma unroll
+          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+            u32x4 ka2;
+            if constexpr (C::kTr)
+              ka2 = tr_chunk(b + C::KN, C::NROW, 32 * sb, ob, ci, lane);
+            else
+              ka2 = keyrow_chunk<T>(b + C::KT + (32 * ob + l32) * C::TROW + 32 * sb * C::S, ci, h);
+            dq[ob] = Elt<T>::mma(ka2, dsc.c[ci], dq[ob]);
+          }
+        }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow < n) {
+    char* dqrow = reinterpret_cast<char*>(dQ + (head + qrow) * D);
+#pragma unroll
+    for (int ob = 0; ob < C::NOB; ++ob)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = 32 * ob + 8 * g + 4 * h;
+        if (a0 < D) {
+          if constexpr (C::S == 2) {
+            u32x2 w = {Elt<T>::pack2(dq[ob][4 * g] * scale, dq[ob][4 * g + 1] * scale),
+                       Elt<T>::pack2(dq[ob][4 * g + 2] * scale, dq[ob][4 * g + 3] * scale)};
+            *reinterpret_cast<u32x2*>(dqrow + a0 * C::S) = w;
+          } else {
+            f32x4 w = {dq[ob][4 * g] * scale, dq[ob][4 * g + 1] * scale,
+                       dq[ob][4 * g + 2] * scale, dq[ob][4 * g + 3] * scale};
+            *reinterpret_cast<f32x4*>(dqrow + a0 * C::S) = w;
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ launch
+// ---------------------------------------------------------------------------
+template <typename T, int D, int MASK, bool DROP>
+static hipError_t launch_dq_t(const BwdArgs& a) {
+  using C = DqCfg<T, D>;
+  const int num_qtiles = (int)((a.n + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, MASK, DROP>),
+                     dim3((unsigned)(num_qtiles * a.bh)), dim3(C::kThreads), 0, a.stream,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
+                     static_cast<const T*>(a.o), a.lse, a.delta, static_cast<T*>(a.dq),
+                     (int)a.n, (int)a.bh, num_qtiles, (int)a.window, a.qk_scale, a.qmode,
+                     a.scale, a.drop);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int MASK>
+static hipError_t launch_dq_m(const BwdArgs& a) {
+  return a.drop.thr > 0 ? launch_dq_t<T, D, MASK, true>(a) : launch_dq_t<T, D, MASK, false>(a);
+}
+
+template <typename T, int D>
+static hipError_t launch_dq_d(const BwdArgs& a) {
+  switch (a.mask) {
+    case 0: return launch_dq_m<T, D, 0>(a);
+    case 1: return launch_dq_m<T, D, 1>(a);
+    default: return launch_dq_m<T, D, 2>(a);
+  }
+}
+
+template <typename T>
+static hipError_t launch_dq_dt(const BwdArgs& a) {
+  switch (a.d) {
+    case 16: return launch_dq_d<T, 16>(a);
+    case 64: return launch_dq_d<T, 64>(a);
+    default: return launch_dq_d<T, 128>(a);
+  }
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  switch (a.dtype) {
+    case 0: return launch_dq_dt<float>(a);
+    case 1: return launch_dq_dt<_Float16>(a);
+    default: return launch_dq_dt<__bf16>(a);
+  }
+}
+
+}  // namespace eiat

@@ -279,14 +279,16 @@ struct TileLoader {
     const uint32_t m0base = (uint32_t)(uintptr_t)(lds_char_t)(lds_tile + 1024 * wave);
     // A tile that runs past row n - 1 clamps every lane's offset to the last
     // chunk of that row: rows past n then hold copies of earlier rows' data
-    // (in bounds, finite), which the kernels mask or weight by zero.
-    const uint32_t lim =
-        r0 + R > n ? (uint32_t)((n - r0) * (C * 16) - 16) : 0xFFFFFFFFu;
-    issue<0>(g, m0base, lim, wave, lane);
+    // (in bounds, finite), which the kernels mask or weight by zero.  Whole
+    // tiles (all but the last of a head) take the offsets as they are.
+    if (r0 + R > n)
+      issue<0, true>(g, m0base, (uint32_t)((n - r0) * (C * 16) - 16), wave, lane);
+    else
+      issue<0, false>(g, m0base, 0u, wave, lane);
   }
 
  private:
-  template <int K>
+  template <int K, bool CLAMP>
   __device__ inline void issue(const char* g, uint32_t m0base, uint32_t lim, int wave,
                                int lane) const {
     if constexpr (K < kPer) {
@@ -295,7 +297,7 @@ struct TileLoader {
       // past the end for some waves (wave < WAVES)
       if (K + 1 < kPer || kInstr % WAVES == 0 || i < kInstr) {
         if (kSlots % 64 == 0 || 64 * i + lane < kSlots) {
-          const uint32_t o = min(off[K], lim);
+          const uint32_t o = CLAMP ? min(off[K], lim) : off[K];
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
           asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -305,7 +307,7 @@ struct TileLoader {
 #pragma clang diagnostic pop
         }
       }
-      issue<K + 1>(g, m0base, lim, wave, lane);
+      issue<K + 1, CLAMP>(g, m0base, lim, wave, lane);
     }
   }
 };

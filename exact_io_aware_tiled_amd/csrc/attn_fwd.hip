@@ -401,12 +401,22 @@ __global__ void
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) {
         if (!active(sb, masked)) continue;
+        // Only a block that some row of the wave sees in part needs the
+        // per-element mask (on the causal diagonal one block per wave);
+        // blocks whose 32 keys every row of the wave sees are taken whole.
+        const int jb = j0 + 32 * sb;
+        bool whole = jb + 31 < n;
+        if constexpr (MASK != 0) whole = whole && jb + 31 <= qw0;
+        if constexpr (MASK == 2) whole = whole && jb >= qw0 + 31 - window + 1;
+        if (!whole) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (!key_allowed<MASK>(qrow, j, n, window)) s[sb][e] = -INFINITY;
-          m4[e & 3] = fmaxf(m4[e & 3], s[sb][e]);
+          for (int e = 0; e < 16; ++e) {
+            const int j = jb + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (!key_allowed<MASK>(qrow, j, n, window)) s[sb][e] = -INFINITY;
+          }
         }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], s[sb][e]);
       }
       mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     } else {
@@ -549,13 +559,14 @@ __global__ void
   // at the top, are stored for the next iteration.  With one score buffer
   // S_{t+1} overwrites S_t after its exponentials (the scheduler interleaves
   // those MFMAs with the second half of the tile); with two (d = 128, twice
-  // the MFMA work per tile) S_{t+1} is issued first into the second buffer and
-  // moved to the first at the end of the iteration.
-  auto iterate = [&](int t, auto masked) __attribute__((always_inline)) {
+  // the MFMA work per tile) S_{t+1} is issued first into the other buffer.
+  // cur holds S_t; nxt receives S_{t+1} (the same buffer below d = 128).
+  auto iterate = [&](int t, f32x16 (&cur)[C::NSB], f32x16 (&nxt)[C::NSB], auto masked)
+      __attribute__((always_inline)) {
     const bool has1 = t + 1 < t_hi, has2 = t + 2 < t_hi;
     if (has1) load_v(t + 1);
     if (has2) load_k(t + 2);
-    const float m_use = prep_tile(t, sc[0], masked);
+    const float m_use = prep_tile(t, cur, masked);
     // Raised priority while this wave has MFMAs to issue, so another wave's
     // softmax VALU work fills the gaps rather than delaying them.
     __builtin_amdgcn_s_setprio(1);
@@ -576,11 +587,11 @@ __global__ void
       }
     };
     if constexpr (C::kDoubleS) {
-      next_scores(sc[C::kDoubleS ? 1 : 0]);
-      exp_pv_tile(t, sc[0], m_use, masked);
+      next_scores(nxt);
+      exp_pv_tile(t, cur, m_use, masked);
     } else {
-      exp_pv_tile(t, sc[0], m_use, masked);
-      next_scores(sc[0]);
+      exp_pv_tile(t, cur, m_use, masked);
+      next_scores(nxt);
     }
     __builtin_amdgcn_s_setprio(0);
     if constexpr (F8 != 0) {
@@ -597,13 +608,32 @@ __global__ void
     }
     advance_ksw();
     __syncthreads();
-    if constexpr (C::kDoubleS) {
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) sc[0][sb] = sc[C::kDoubleS ? 1 : 0][sb];
-    }
   };
+  // With two score buffers the loop is unrolled by two so that the buffers
+  // swap roles without copies; `swapped` says S_t sits in sc[1] (a segment
+  // that ends after an odd number of tiles), which the next segment undoes
+  // with one copy.
+  constexpr int kB = C::kDoubleS ? 1 : 0;
+  bool swapped = false;
   auto run = [&](int t, int end, auto masked) __attribute__((always_inline)) -> int {
-    for (; t < end; ++t) iterate(t, masked);
+    if constexpr (C::kDoubleS) {
+      if (t < end && swapped) {
+#pragma unroll
+        for (int sb = 0; sb < C::NSB; ++sb) sc[0][sb] = sc[kB][sb];
+        swapped = false;
+      }
+      for (; t + 1 < end; t += 2) {
+        iterate(t, sc[0], sc[kB], masked);
+        iterate(t + 1, sc[kB], sc[0], masked);
+      }
+      if (t < end) {
+        iterate(t, sc[0], sc[kB], masked);
+        ++t;
+        swapped = true;
+      }
+    } else {
+      for (; t < end; ++t) iterate(t, sc[0], sc[0], masked);
+    }
     return t;
   };
   int t = run(t_lo, t_in_lo, std::true_type{});
