@@ -67,7 +67,11 @@ struct DkvCfg {
   // 16-bit: Q^T and dO^T operands come from the natural tiles through transpose
   // reads; float32 keeps transposed copies.
   static constexpr bool kTr = (S == 2);
-  static constexpr int NROW = (kTr ? DP : D) * S + 16;  // Q / dO natural rows
+  // 16-byte padding slots per row: two at 16-bit d = 128 (conflict-free
+  // transposing reads of Q^T and dO^T over the 64 LDS banks); one below, where
+  // two workgroups per CU would not fit the wider rows.
+  static constexpr int PAD = (kTr && D >= 128) ? 2 : 1;
+  static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // Q / dO natural rows
   static constexpr int TROW = BMQ * S + 16;             // Q^T / dO^T rows (float32)
   static constexpr int TBYTES = kTr ? 0 : DP * TROW;
   static constexpr int QN = 0;
@@ -133,7 +137,8 @@ __global__ void __launch_bounds__(256)
     if (qmode == 2) kf[c] = zero4();  // c = 0: every score is exactly 0
   }
   if constexpr (C::kVLds)
-    tile_to_lds<32, D * C::S / 16, 1>(smem + C::VRES + 32 * wave * C::NROW, Vh, kw0, n, 0, lane);
+    tile_to_lds<32, D * C::S / 16, 1, C::PAD>(smem + C::VRES + 32 * wave * C::NROW, Vh, kw0, n, 0,
+                                               lane);
 
   // Query rows that may see any key of this workgroup.
   int qbeg = 0, qend = n;
@@ -161,7 +166,7 @@ __global__ void __launch_bounds__(256)
     }
   }
 
-  TileLoader<BMQ, D * C::S / 16, C::kWaves> tl;
+  TileLoader<BMQ, D * C::S / 16, C::kWaves, C::PAD> tl;
   if constexpr (C::kDirect) tl.init(wave, lane);
   St sq, so;
   float4 lreg, dreg;  // LSE and delta of 4 rows as loaded (threads < BMQ / 4)

@@ -30,7 +30,11 @@ struct DqCfg {
   // 16-bit: the K^T operand comes from the natural K tile through transpose
   // reads; float32 keeps a transposed copy.
   static constexpr bool kTr = (S == 2);
-  static constexpr int NROW = (kTr ? DP : D) * S + 16;  // K, V natural rows
+  static constexpr bool kDirect = kTr && D >= 32;
+  // 16-byte padding slots per row: two for direct-loaded 16-bit tiles, so the
+  // transposing reads of K^T use all 64 LDS banks without conflicts.
+  static constexpr int PAD = kDirect ? 2 : 1;
+  static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // K, V natural rows
   static constexpr int TROW = BN * S + 16;              // K^T rows (float32)
   static constexpr int KN = 0;
   static constexpr int KT = KN + BN * NROW;
@@ -39,7 +43,6 @@ struct DqCfg {
   static constexpr int NCH = D * S / 32;
   static constexpr int NOB = DP / 32;
   static constexpr int NSB = BN / 32;
-  static constexpr bool kDirect = kTr && D >= 32;
 };
 
 template <typename T, int D, int MASK, bool DROP>
@@ -120,7 +123,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
       zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + b * C::BUF + C::KT, tid);
   }
 
-  TileLoader<BN, D * C::S / 16, C::kWaves> tl;
+  TileLoader<BN, D * C::S / 16, C::kWaves, C::PAD> tl;
   if constexpr (C::kDirect) tl.init(wave, lane);
   StK sk;
   StV sv;

@@ -197,7 +197,7 @@ __device__ inline u32x4 fp8_negate(u32x4 w) {
 }
 
 // Copy rows [r0, r0 + R) of a [n][C * 16 bytes] global slice into an LDS tile
-// whose rows are C 16-byte chunks plus one padding chunk, with the gfx950
+// whose rows are C 16-byte chunks plus PAD padding chunks, with the gfx950
 // direct-to-LDS load (global_load_lds_dwordx4): wave instruction i writes the
 // 1 KiB [1024 i, 1024 i + 1024) of the tile, lane l its 16-byte slot 64 i + l
 // (placement checked on the GPU).  Slots map onto whole rows; a padding slot
@@ -227,10 +227,10 @@ __device__ inline void lds_dma16(const char* src, char* lds_dst) {
 #pragma clang diagnostic pop
 }
 
-template <int R, int C, int WAVES>
+template <int R, int C, int WAVES, int PAD = 1>
 __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, int n, int wave,
                                    int lane) {
-  constexpr int kSlots = R * (C + 1);
+  constexpr int kSlots = R * (C + PAD);
   constexpr int kInstr = (kSlots + 63) / 64;
 #pragma unroll
   for (int i0 = 0; i0 < kInstr; i0 += WAVES) {
@@ -238,7 +238,7 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
     if (i0 + WAVES <= kInstr || i < kInstr) {  // wave < WAVES
       const int slot = 64 * i + lane;
       if (kSlots % 64 == 0 || slot < kSlots) {
-        const int row = slot / (C + 1), c = slot % (C + 1);
+        const int row = slot / (C + PAD), c = slot % (C + PAD);
         const int gr = min(r0 + row, n - 1);
         const char* src = gbase + (int64_t)gr * (C * 16) + (c < C ? c : 0) * 16;
         lds_dma16(src, lds_tile + 1024 * i);
@@ -253,9 +253,9 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
 // (init).  Per tile only scalar arithmetic and one min per instruction (the
 // clamp of a tile that runs past row n - 1) change.  `wave` must be
 // wave-uniform (e.g. from readfirstlane).
-template <int R, int C, int WAVES>
+template <int R, int C, int WAVES, int PAD = 1>
 struct TileLoader {
-  static constexpr int kSlots = R * (C + 1);
+  static constexpr int kSlots = R * (C + PAD);
   static constexpr int kInstr = (kSlots + 63) / 64;
   static constexpr int kPer = (kInstr + WAVES - 1) / WAVES;
   uint32_t off[kPer];
@@ -264,7 +264,7 @@ struct TileLoader {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int slot = 64 * (k * WAVES + wave) + lane;
-      const int row = slot / (C + 1), c = slot % (C + 1);
+      const int row = slot / (C + PAD), c = slot % (C + PAD);
       off[k] = (uint32_t)(row * (C * 16) + (c < C ? c : 0) * 16);
     }
   }

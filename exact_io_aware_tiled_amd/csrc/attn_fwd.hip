@@ -67,9 +67,14 @@ struct FwdCfg {
   static constexpr int S = Elt<T>::kBytes;
   static constexpr bool kTr = (S == 2);       // 16-bit: V row-major + transpose reads
   static constexpr int KS = F8 ? 1 : S;       // bytes per Q / K element (FP8 scores: 1)
-  static constexpr int KROW = D * KS + 16;    // K tile row stride in LDS (bytes), padded
+  // 16-byte padding slots per LDS tile row.  16-bit tiles loaded directly
+  // take two (rows of 2 d + 32 bytes), so that the transposing reads of a V
+  // tile (8 rows x 64 bytes per instruction) spread over all 64 LDS banks
+  // without conflicts, as the 16-byte row reads of a K tile do with either.
+  static constexpr int PAD = (kTr && D >= 32 && !F8) ? 2 : 1;
+  static constexpr int KROW = D * KS + 16 * PAD;  // K tile row stride in LDS (bytes), padded
   // V tile: row-major [BN][DP] (16-bit) or transposed [DP][BN] (float32)
-  static constexpr int VROW = F8 == 2 ? 64 + 16 : (kTr ? DP * S + 16 : BN * S + 16);
+  static constexpr int VROW = F8 == 2 ? 64 + 16 : (kTr ? DP * S + 16 * PAD : BN * S + 16);
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = (kTr && F8 != 2 ? BN : DP) * VROW;
   static constexpr int NCH = D * S / 32;      // d-chunks per 32x32 product (both halves)
@@ -217,7 +222,7 @@ __global__ void
     }
   }
 
-  TileLoader<BN, C::CPR, C::kWaves> tl;
+  TileLoader<BN, C::CPR, C::kWaves, C::PAD> tl;
   TileLoader<D, 4, C::kWaves> tlv;  // FP8 values: D rows of 64 codes
   if constexpr (F8 == 2) tlv.init(wave, lane);
   // FP8 values: scale words of the V^T rows this lane supplies (block h of
