@@ -45,13 +45,23 @@ def header_functions() -> list[str]:
 def load_library():
     """Load libeiat_attn.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+def load_check_library(name: str):
+    """One of the check builds (``poison`` or ``alt``, see build.CHECK_BUILDS):
+    the same C ABI compiled with a checking macro, for tests only."""
+    return _open(os.path.join(HERE, f"libeiat_attn_{name}.so"))
+
+
+def _open(path: str):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
             "or `python exact_io_aware_tiled_amd/build.py`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path, mode=os.RTLD_LOCAL)
     vp, i64, c_int, c_float = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, c_int, c_float, c_int,
                              i64, vp]
@@ -96,7 +106,6 @@ def load_library():
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
     lib.attn_abi_version.restype = c_int
-    _lib = lib
     return lib
 
 

@@ -47,8 +47,26 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+# Check builds, used only by tests (tests/test_check_builds_gpu.py): the same
+# ABI compiled with a macro of csrc/attn_device.h into a library of its own.
+# Each recompiles the sources that the macro changes and links the rest of the
+# product build's objects.
+#   libeiat_attn_poison.so  EIAT_LDS_POISON: every direct HBM -> LDS load
+#                           first fills its destination with NaN
+#   libeiat_attn_alt.so     EIAT_ALT_TILES: other tile shapes
+CHECK_BUILDS = {
+    "poison": (["-DEIAT_LDS_POISON"],
+               ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_decode.hip"]),
+    "alt": (["-DEIAT_ALT_TILES"], ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]),
+}
+
+
+def check_lib_path(name: str) -> str:
+    return os.path.join(HERE, f"libeiat_attn_{name}.so")
+
+
+def _compile(src: str, extra: list[str], objdir: str = OBJ) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *CFLAGS, *PER_SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
            "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,20 +75,42 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    extra = list(extra or [])
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
            "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, checks: bool = True) -> str:
+    """Compile the product library (and, with `checks`, the check builds) for gfx950."""
+    os.makedirs(OBJ, exist_ok=True)
+    extra = list(extra or [])
+    jobs = [(src, extra, OBJ) for src in SOURCES]
+    if checks:
+        for name, (flags, srcs) in CHECK_BUILDS.items():
+            d = os.path.join(OBJ, name)
+            os.makedirs(d, exist_ok=True)
+            jobs += [(src, extra + flags, d) for src in srcs]
+    # the forward units (the slowest) first
+    jobs.sort(key=lambda j: j[0] != "attn_fwd.hip")
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    base = {src: os.path.join(OBJ, os.path.splitext(src)[0] + ".o") for src in SOURCES}
+    _link([base[s] for s in SOURCES], LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
+    if checks:
+        for name, (_, srcs) in CHECK_BUILDS.items():
+            d = os.path.join(OBJ, name)
+            objs = [os.path.join(d, os.path.splitext(s)[0] + ".o") if s in srcs else base[s]
+                    for s in SOURCES]
+            _link(objs, check_lib_path(name))
+            if verbose:
+                print(f"built {check_lib_path(name)}", file=sys.stderr)
     return LIB
 
 

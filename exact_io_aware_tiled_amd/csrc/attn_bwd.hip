@@ -61,7 +61,8 @@ struct DkvCfg {
   // the barriers per query row and four 32-row blocks of independent MFMA work
   // per tile (8 % faster than 64 rows at d = 64; the LDS still fits two
   // workgroups per CU).  d = 128 keeps 32 rows so two workgroups fit with V in LDS.
-  static constexpr int BMQ = D >= 128 ? 32 : (Elt<T>::kBytes == 2 ? 128 : 64);
+  // (The tile-shape check build streams 64-row tiles at 16-bit d <= 64.)
+  static constexpr int BMQ = D >= 128 ? 32 : (Elt<T>::kBytes == 2 && !kAltTiles ? 128 : 64);
   static constexpr int DP = D < 32 ? 32 : D;
   static constexpr int S = Elt<T>::kBytes;
   // 16-bit: Q^T and dO^T operands come from the natural tiles through transpose

@@ -25,7 +25,8 @@ struct DqCfg {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 32 * kWaves;
   static constexpr int S = Elt<T>::kBytes;
-  static constexpr int BN = (S == 4 && D >= 128) ? 32 : 64;  // keys per streamed tile
+  // keys per streamed tile (the tile-shape check build: 32 for 16-bit types)
+  static constexpr int BN = ((S == 4 && D >= 128) || (S == 2 && kAltTiles)) ? 32 : 64;
   static constexpr int DP = D < 32 ? 32 : D;
   // 16-bit: the K^T operand comes from the natural K tile through transpose
   // reads; float32 keeps a transposed copy.

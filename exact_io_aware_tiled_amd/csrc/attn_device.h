@@ -196,6 +196,35 @@ __device__ inline u32x4 fp8_negate(u32x4 w) {
   return w;
 }
 
+// Check builds (compiled into separate libraries; never the product path):
+//   EIAT_LDS_POISON  every direct HBM -> LDS load first fills the 16 bytes its
+//                    lane will write with all-ones (a NaN in every element
+//                    type), so a tile read before its loads have landed and
+//                    been published by a barrier shows up as non-finite or
+//                    changed output; a correctly synchronized kernel gives
+//                    bitwise the results of the normal build.
+//   EIAT_ALT_TILES   other tile shapes (keys per streamed tile, query rows per
+//                    dK/dV tile), for the check that results do not depend on
+//                    the block size beyond rounding.
+#ifdef EIAT_ALT_TILES
+constexpr bool kAltTiles = true;
+#else
+constexpr bool kAltTiles = false;
+#endif
+
+// Poison check build: fill this lane's 16-byte slot at LDS address `lds` and
+// wait for the write, before a direct load is issued into it.
+__device__ inline void poison_lds_slot(uint32_t lds) {
+#ifdef EIAT_LDS_POISON
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  const u32x4 ones = {~0u, ~0u, ~0u, ~0u};
+  *reinterpret_cast<lds_u32x4*>((uintptr_t)lds) = ones;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+  (void)lds;
+#endif
+}
+
 // Copy rows [r0, r0 + R) of a [n][C * 16 bytes] global slice into an LDS tile
 // whose rows are C 16-byte chunks plus PAD padding chunks, with the gfx950
 // direct-to-LDS load (global_load_lds_dwordx4): wave instruction i writes the
@@ -218,6 +247,7 @@ __device__ inline void lds_dma16(const char* src, char* lds_dst) {
   typedef char __attribute__((address_space(3)))* lds_char_t;
   const uint32_t base =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t)lds_dst);
+  poison_lds_slot(base + 16 * (threadIdx.x & 63));
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -298,6 +328,7 @@ struct TileLoader {
       if (K + 1 < kPer || kInstr % WAVES == 0 || i < kInstr) {
         if (kSlots % 64 == 0 || 64 * i + lane < kSlots) {
           const uint32_t o = CLAMP ? min(off[K], lim) : off[K];
+          poison_lds_slot(m0base + 1024 * WAVES * K + 16 * lane);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
           asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"

@@ -62,7 +62,10 @@ struct FwdCfg {
   // and loop overhead per key, four independent 32-key score blocks per tile
   // (4-7 % faster at d = 64 although the 72 KiB of tiles leave room for two
   // workgroups per CU instead of three).
-  static constexpr int BN = (D == 64 && Elt<T>::kBytes == 2 && !F8) ? 128 : 64;
+  // (The tile-shape check build takes 64 keys at d = 64 and 32 at d = 128.)
+  static constexpr int BN = (Elt<T>::kBytes == 2 && !F8)
+                                ? (kAltTiles ? (D == 128 ? 32 : 64) : (D == 64 ? 128 : 64))
+                                : 64;
   static constexpr int DP = D < 32 ? 32 : D;  // value rows padded to whole 32-row blocks
   static constexpr int S = Elt<T>::kBytes;
   static constexpr bool kTr = (S == 2);       // 16-bit: V row-major + transpose reads

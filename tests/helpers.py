@@ -69,8 +69,13 @@ def check_fwd(o_gpu, lse_gpu, y_ref, lse_ref, dtype, what="", score_scale: float
     return err_o, err_l
 
 
-def check_grad(g_gpu, g_ref, dtype, what=""):
-    """Per (b, h) slice: max |err| / max |ref| (16-bit) or max |err| (fp32, scaled)."""
+def check_grad(g_gpu, g_ref, dtype, what="", unit_scores: bool = False):
+    """Per (b, h) slice: max |err| / max |ref| (16-bit) or max |err| (fp32).
+
+    float32: 1e-5 * max(1, max |ref|) in general, the flat 1e-5 when
+    `unit_scores` (c = 1/sqrt(d) on N(0, 1) rows, the scores of the workloads);
+    tests/test_fp32_envelope.py shows a plain float32 evaluation needs the
+    scaled form once the scores or gradients are large."""
     assert np.all(np.isfinite(g_gpu)), f"{what}: non-finite gradient"
     g_gpu = g_gpu.reshape(-1, *g_gpu.shape[-2:])
     g_ref = g_ref.reshape(-1, *g_ref.shape[-2:])
@@ -79,7 +84,7 @@ def check_grad(g_gpu, g_ref, dtype, what=""):
         err = float(np.max(np.abs(g_gpu[s] - g_ref[s])))
         ref = max(float(np.max(np.abs(g_ref[s]))), GRAD_FLOOR)
         if dtype == torch.float32:
-            bound = TOL_GRAD_F32 * max(1.0, ref)
+            bound = TOL_GRAD_F32 if unit_scores else TOL_GRAD_F32 * max(1.0, ref)
             assert err <= bound, f"{what}[{s}]: max abs err {err:.3g} > {bound:.3g}"
             worst = max(worst, err / max(1.0, ref))
         else:
