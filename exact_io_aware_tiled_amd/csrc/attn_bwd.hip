@@ -68,10 +68,13 @@ struct DkvCfg {
   // 16-bit: Q^T and dO^T operands come from the natural tiles through transpose
   // reads; float32 keeps transposed copies.
   static constexpr bool kTr = (S == 2);
-  // 16-byte padding slots per row: two at 16-bit d = 128 (conflict-free
-  // transposing reads of Q^T and dO^T over the 64 LDS banks); one below, where
-  // two workgroups per CU would not fit the wider rows.
-  static constexpr int PAD = (kTr && D >= 128) ? 2 : 1;
+  // Bank conflicts of the Q / dO tiles: at 16-bit d = 128 rows padded by two
+  // 16-byte slots (conflict-free transposing reads of Q^T and dO^T over the
+  // 64 LDS banks); at 16-bit d = 64, where two workgroups per CU would not fit
+  // such rows, unpadded rows with chunks XOR-swizzled (swz_chunk), equally
+  // conflict-free; one padding slot otherwise.
+  static constexpr bool kSwz = kTr && D == 64;
+  static constexpr int PAD = (kTr && D >= 128) ? 2 : (kSwz ? 0 : 1);
   static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // Q / dO natural rows
   static constexpr int TROW = BMQ * S + 16;             // Q^T / dO^T rows (float32)
   static constexpr int TBYTES = kTr ? 0 : DP * TROW;
@@ -167,8 +170,10 @@ __global__ void __launch_bounds__(256)
     }
   }
 
-  TileLoader<BMQ, D * C::S / 16, C::kWaves, C::PAD> tl;
+  TileLoader<BMQ, D * C::S / 16, C::kWaves, C::PAD, C::kSwz> tl;
   if constexpr (C::kDirect) tl.init(wave, lane);
+  SwzReads swz;
+  if constexpr (C::kSwz) swz.init(lane);
   St sq, so;
   float4 lreg, dreg;  // LSE and delta of 4 rows as loaded (threads < BMQ / 4)
   int lrow0 = 0;      // first row of the tile those loads belong to
@@ -289,8 +294,14 @@ __global__ void __launch_bounds__(256)
           const int rq = 32 * qb + l32;
   #pragma unroll
           for (int c = 0; c < C::NCH; ++c) {
-            u32x4 qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
-            u32x4 oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
+            u32x4 qa, oa;
+            if constexpr (C::kSwz) {
+              qa = swz.row_read(b + C::QN, 32 * qb, c);
+              oa = swz.row_read(b + C::ON, 32 * qb, c);
+            } else {
+              qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
+              oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
+            }
             s = Elt<T>::mma(qa, kf[c], s);
             u32x4 vb4;
             if constexpr (C::kVLds)
@@ -357,8 +368,13 @@ __global__ void __launch_bounds__(256)
             for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
               u32x4 oa, qa2;
               if constexpr (C::kTr) {
-                oa = tr_chunk(b + C::ON, C::NROW, 32 * qb, ob, ci, lane);
-                qa2 = tr_chunk(b + C::QN, C::NROW, 32 * qb, ob, ci, lane);
+                if constexpr (C::kSwz) {
+                  oa = swz.tr_read(b + C::ON, 32 * qb, ob, ci);
+                  qa2 = swz.tr_read(b + C::QN, 32 * qb, ob, ci);
+                } else {
+                  oa = tr_chunk(b + C::ON, C::NROW, 32 * qb, ob, ci, lane);
+                  qa2 = tr_chunk(b + C::QN, C::NROW, 32 * qb, ob, ci, lane);
+                }
               } else {
                 oa = keyrow_chunk<T>(b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
                 qa2 = keyrow_chunk<T>(b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);

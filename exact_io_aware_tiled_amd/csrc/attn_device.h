@@ -283,8 +283,22 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
 // (init).  Per tile only scalar arithmetic and one min per instruction (the
 // clamp of a tile that runs past row n - 1) change.  `wave` must be
 // wave-uniform (e.g. from readfirstlane).
-template <int R, int C, int WAVES, int PAD = 1>
+// XOR swizzle of unpadded 128-byte LDS rows (8 chunks of 16 bytes): chunk c
+// of tile row r is stored in slot c ^ swz_chunk(r), where swz_chunk takes bits
+// 1..3 of r and swaps the two upper ones.  Then both read patterns of a 16-bit
+// d = 64 tile spread over all 64 LDS banks without conflicts: 16-byte reads
+// of one chunk in 32 consecutive rows, and transposing reads of 8 rows x 64
+// bytes (by a bank model of the two patterns; padding would do the same but
+// needs 32 bytes per row).  Rows that differ by a multiple of 16 share the
+// pattern.
+__device__ inline int swz_chunk(int r) {
+  const int p = (r >> 1) & 7;
+  return (p & 1) | ((p & 2) << 1) | ((p & 4) >> 1);
+}
+
+template <int R, int C, int WAVES, int PAD = 1, bool SWZ = false>
 struct TileLoader {
+  static_assert(!SWZ || (C == 8 && PAD == 0), "swizzled tiles: unpadded 128-byte rows");
   static constexpr int kSlots = R * (C + PAD);
   static constexpr int kInstr = (kSlots + 63) / 64;
   static constexpr int kPer = (kInstr + WAVES - 1) / WAVES;
@@ -295,7 +309,10 @@ struct TileLoader {
     for (int k = 0; k < kPer; ++k) {
       const int slot = 64 * (k * WAVES + wave) + lane;
       const int row = slot / (C + PAD), c = slot % (C + PAD);
-      off[k] = (uint32_t)(row * (C * 16) + (c < C ? c : 0) * 16);
+      // the slot's global chunk: the slot's own (swizzled tiles: the chunk
+      // stored there), a padding slot a duplicate of chunk 0
+      const int gc = SWZ ? (c ^ swz_chunk(row)) : (c < C ? c : 0);
+      off[k] = (uint32_t)(row * (C * 16) + gc * 16);
     }
   }
 
@@ -369,6 +386,42 @@ __device__ inline u32x4 tr_chunk(const char* vtile, int vrow_bytes, int kbase, i
   u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
   return r;
 }
+
+// The reads of a swizzled 128-byte-row tile (swz_chunk): offsets fixed per
+// lane, computed once.  row_read: the 16-byte A-operand chunk c (0..3) of row
+// r0 + L % 32, half h, as *(tile + 128 r0 + row[c]) (r0 a multiple of 16).
+// tr_read: what tr_chunk(tile, 128, kbase, ob, ci, lane) reads from an
+// unswizzled tile (kbase a multiple of 16).
+struct SwzReads {
+  uint32_t row[4];
+  uint32_t tr[2][2];
+  __device__ inline void init(int lane) {
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) row[c] = 128 * l32 + 16 * ((2 * c + h) ^ swz_chunk(l32));
+    const int G = lane >> 4, j = lane & 15;
+    const int y = 2 * (G & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int rr = 4 * (G >> 1) + (j >> 2) + 8 * r;
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob)
+        tr[r][ob] = 128 * rr + 16 * ((4 * ob + y) ^ swz_chunk(rr)) + 8 * (j & 1);
+    }
+  }
+  __device__ inline u32x4 row_read(const char* tile, int r0, int c) const {
+    return *reinterpret_cast<const u32x4*>(tile + 128 * r0 + row[c]);
+  }
+  __device__ inline u32x4 tr_read(const char* tile, int kbase, int ob, int ci) const {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const char* base = tile + 128 * (kbase + 16 * ci);
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + tr[0][ob]));
+    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + tr[1][ob]));
+    u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    u32x4 r = {ua[0], ua[1], ub[0], ub[1]};
+    return r;
+  }
+};
 
 // The value held by lane L ^ 32.  v_permlane32_swap exchanges the upper half of
 // its first operand with the lower half of its second; with both operands equal
