@@ -68,13 +68,11 @@ struct DkvCfg {
   // 16-bit: Q^T and dO^T operands come from the natural tiles through transpose
   // reads; float32 keeps transposed copies.
   static constexpr bool kTr = (S == 2);
-  // Bank conflicts of the Q / dO tiles: at 16-bit d = 128 rows padded by two
-  // 16-byte slots (conflict-free transposing reads of Q^T and dO^T over the
-  // 64 LDS banks); at 16-bit d = 64, where two workgroups per CU would not fit
-  // such rows, unpadded rows with chunks XOR-swizzled (swz_chunk), equally
-  // conflict-free; one padding slot otherwise.
+  // LDS bank conflicts of the Q / dO tiles (and of the resident V rows):
+  // swizzled unpadded rows at 16-bit d = 64, three padding slots at 16-bit
+  // d = 128, one otherwise (as the forward's tiles, attn_fwd.hip).
   static constexpr bool kSwz = kTr && D == 64;
-  static constexpr int PAD = (kTr && D >= 128) ? 2 : (kSwz ? 0 : 1);
+  static constexpr int PAD = kSwz ? 0 : ((kTr && D >= 128) ? 3 : 1);
   static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // Q / dO natural rows
   static constexpr int TROW = BMQ * S + 16;             // Q^T / dO^T rows (float32)
   static constexpr int TBYTES = kTr ? 0 : DP * TROW;

@@ -32,9 +32,11 @@ struct DqCfg {
   // reads; float32 keeps a transposed copy.
   static constexpr bool kTr = (S == 2);
   static constexpr bool kDirect = kTr && D >= 32;
-  // 16-byte padding slots per row: two for direct-loaded 16-bit tiles, so the
-  // transposing reads of K^T use all 64 LDS banks without conflicts.
-  static constexpr int PAD = kDirect ? 2 : 1;
+  // LDS bank conflicts of the K and V tiles: swizzled unpadded rows at 16-bit
+  // d = 64, three padding slots at 16-bit d = 128, one otherwise (as the
+  // forward's tiles, attn_fwd.hip).
+  static constexpr bool kSwz = kDirect && D == 64;
+  static constexpr int PAD = kSwz ? 0 : ((kDirect && D >= 128) ? 3 : 1);
   static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // K, V natural rows
   static constexpr int TROW = BN * S + 16;              // K^T rows (float32)
   static constexpr int KN = 0;
@@ -124,8 +126,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
       zero_pad_rows<D, C::DP, C::TROW, C::kThreads>(smem + b * C::BUF + C::KT, tid);
   }
 
-  TileLoader<BN, D * C::S / 16, C::kWaves, C::PAD> tl;
+  TileLoader<BN, D * C::S / 16, C::kWaves, C::PAD, C::kSwz> tl;
   if constexpr (C::kDirect) tl.init(wave, lane);
+  SwzReads swz;
+  if constexpr (C::kSwz) swz.init(lane);
   StK sk;
   StV sv;
   auto load_tile = [&](int t) {
@@ -181,8 +185,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
         const int rk = 32 * sb + l32;
 #pragma unroll
         for (int c = 0; c < C::NCH; ++c) {
-          u32x4 ka = *reinterpret_cast<const u32x4*>(b + C::KN + rk * C::NROW + 32 * c + 16 * h);
-          u32x4 va = *reinterpret_cast<const u32x4*>(b + C::VN + rk * C::NROW + 32 * c + 16 * h);
+          u32x4 ka, va;
+          if constexpr (C::kSwz) {
+            ka = swz.row_read(b + C::KN, 32 * sb, c);
+            va = swz.row_read(b + C::VN, 32 * sb, c);
+          } else {
+            ka = *reinterpret_cast<const u32x4*>(b + C::KN + rk * C::NROW + 32 * c + 16 * h);
+            va = *reinterpret_cast<const u32x4*>(b + C::VN + rk * C::NROW + 32 * c + 16 * h);
+          }
           s = Elt<T>::mma(ka, qf[c], s);
           dp = Elt<T>::mma(va, of[c], dp);
         }
@@ -220,7 +230,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 #pragma unroll
           for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
             u32x4 ka2;
-            if constexpr (C::kTr)
+            if constexpr (C::kSwz)
+              ka2 = swz.tr_read(b + C::KN, 32 * sb, ob, ci);
+            else if constexpr (C::kTr)
               ka2 = tr_chunk(b + C::KN, C::NROW, 32 * sb, ob, ci, lane);
             else
               ka2 = keyrow_chunk<T>(b + C::KT + (32 * ob + l32) * C::TROW + 32 * sb * C::S, ci, h);

@@ -283,17 +283,21 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
 // (init).  Per tile only scalar arithmetic and one min per instruction (the
 // clamp of a tile that runs past row n - 1) change.  `wave` must be
 // wave-uniform (e.g. from readfirstlane).
-// XOR swizzle of unpadded 128-byte LDS rows (8 chunks of 16 bytes): chunk c
-// of tile row r is stored in slot c ^ swz_chunk(r), where swz_chunk takes bits
-// 1..3 of r and swaps the two upper ones.  Then both read patterns of a 16-bit
-// d = 64 tile spread over all 64 LDS banks without conflicts: 16-byte reads
-// of one chunk in 32 consecutive rows, and transposing reads of 8 rows x 64
-// bytes (by a bank model of the two patterns; padding would do the same but
-// needs 32 bytes per row).  Rows that differ by a multiple of 16 share the
-// pattern.
+// XOR swizzle of unpadded 128-byte LDS rows (d = 64 at 16 bits: 8 chunks of
+// 16 bytes): chunk c of tile row r is stored in slot c ^ swz_chunk(r), with
+// p = bits 1..3 of r and swz_chunk = p rotated right by one bit.  The LDS
+// serves a 16-byte read in passes of 16 lanes and an 8-byte read in passes of
+// 32 lanes, 256 bytes over the 64 banks per pass; with the swizzle both read
+// patterns of these tiles use every bank once per pass: the 16-byte A-operand
+// reads (one chunk of 16 consecutive rows per pass: p runs over all eight
+// values for rows of one parity) and the transposing reads (4 consecutive
+// rows x 64 bytes per pass: rows r and r + 2 land in different halves of the
+// row because bit 1 of r becomes bit 2 of the slot).  Padding cannot do both
+// (a 16-byte pad leaves the transposing reads 2-way conflicted).  The pattern
+// repeats every 16 rows.
 __device__ inline int swz_chunk(int r) {
   const int p = (r >> 1) & 7;
-  return (p & 1) | ((p & 2) << 1) | ((p & 4) >> 1);
+  return ((p & 1) << 2) | (p >> 1);
 }
 
 template <int R, int C, int WAVES, int PAD = 1, bool SWZ = false>

@@ -70,11 +70,13 @@ struct FwdCfg {
   static constexpr int S = Elt<T>::kBytes;
   static constexpr bool kTr = (S == 2);       // 16-bit: V row-major + transpose reads
   static constexpr int KS = F8 ? 1 : S;       // bytes per Q / K element (FP8 scores: 1)
-  // 16-byte padding slots per LDS tile row.  16-bit tiles loaded directly
-  // take two (rows of 2 d + 32 bytes), so that the transposing reads of a V
-  // tile (8 rows x 64 bytes per instruction) spread over all 64 LDS banks
-  // without conflicts, as the 16-byte row reads of a K tile do with either.
-  static constexpr int PAD = (kTr && D >= 32 && !F8) ? 2 : 1;
+  // LDS bank conflicts of the 16-bit tiles loaded directly: at d = 64,
+  // unpadded rows with XOR-swizzled chunks (swz_chunk: conflict-free 16-byte
+  // K reads and transposing V reads); at d = 128 rows padded by three 16-byte
+  // slots (2 d + 48 bytes: conflict-free K reads, transposing reads 2-way,
+  // against 4-way with one slot).  One slot otherwise.
+  static constexpr bool kSwz = kTr && D == 64 && !F8;
+  static constexpr int PAD = kSwz ? 0 : ((kTr && D >= 128 && !F8) ? 3 : 1);
   static constexpr int KROW = D * KS + 16 * PAD;  // K tile row stride in LDS (bytes), padded
   // V tile: row-major [BN][DP] (16-bit) or transposed [DP][BN] (float32)
   static constexpr int VROW = F8 == 2 ? 64 + 16 : (kTr ? DP * S + 16 * PAD : BN * S + 16);
@@ -225,7 +227,9 @@ __global__ void
     }
   }
 
-  TileLoader<BN, C::CPR, C::kWaves, C::PAD> tl;
+  TileLoader<BN, C::CPR, C::kWaves, C::PAD, C::kSwz> tl;
+  SwzReads swz;
+  if constexpr (C::kSwz) swz.init(lane);
   TileLoader<D, 4, C::kWaves> tlv;  // FP8 values: D rows of 64 codes
   if constexpr (F8 == 2) tlv.init(wave, lane);
   // FP8 values: scale words of the V^T rows this lane supplies (block h of
@@ -351,8 +355,11 @@ __global__ void
       } else {
 #pragma unroll
         for (int c = 0; c < C::NCH; ++c) {
-          u32x4 a =
-              *reinterpret_cast<const u32x4*>(kb + (32 * sb + l32) * C::KROW + 32 * c + 16 * h);
+          u32x4 a;
+          if constexpr (C::kSwz)
+            a = swz.row_read(kb, 32 * sb, c);
+          else
+            a = *reinterpret_cast<const u32x4*>(kb + (32 * sb + l32) * C::KROW + 32 * c + 16 * h);
           s[sb] = Elt<T>::mma(a, qf[c], s[sb]);
         }
       }
@@ -511,7 +518,9 @@ __global__ void
 #pragma unroll
         for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
           u32x4 va;
-          if constexpr (C::kTr)
+          if constexpr (C::kSwz)
+            va = swz.tr_read(vb, 32 * sb, ob, ci);
+          else if constexpr (C::kTr)
             va = tr_chunk(vb, C::VROW, 32 * sb, ob, ci, lane);
           else
             va = keyrow_chunk<T>(vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S, ci, h);
