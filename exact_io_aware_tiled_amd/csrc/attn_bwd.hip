@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(256)
 
   TileLoader<BMQ, D * C::S / 16, C::kWaves, C::PAD, C::kSwz> tl;
   if constexpr (C::kDirect) tl.init(wave, lane);
-  SwzReads swz;
+  SwzReads<D == 128 ? 128 : 64> swz;
   if constexpr (C::kSwz) swz.init(lane);
   St sq, so;
   float4 lreg, dreg;  // LSE and delta of 4 rows as loaded (threads < BMQ / 4)

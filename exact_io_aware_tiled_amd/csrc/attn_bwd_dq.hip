@@ -35,8 +35,8 @@ struct DqCfg {
   // LDS bank conflicts of the K and V tiles: swizzled unpadded rows at 16-bit
   // d = 64, three padding slots at 16-bit d = 128, one otherwise (as the
   // forward's tiles, attn_fwd.hip).
-  static constexpr bool kSwz = kDirect && D == 64;
-  static constexpr int PAD = kSwz ? 0 : ((kDirect && D >= 128) ? 3 : 1);
+  static constexpr bool kSwz = kDirect && D >= 64;
+  static constexpr int PAD = kSwz ? 0 : 1;
   static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // K, V natural rows
   static constexpr int TROW = BN * S + 16;              // K^T rows (float32)
   static constexpr int KN = 0;
@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
 
   TileLoader<BN, D * C::S / 16, C::kWaves, C::PAD, C::kSwz> tl;
   if constexpr (C::kDirect) tl.init(wave, lane);
-  SwzReads swz;
+  SwzReads<D> swz;
   if constexpr (C::kSwz) swz.init(lane);
   StK sk;
   StV sv;

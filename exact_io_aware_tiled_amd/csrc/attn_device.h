@@ -295,14 +295,25 @@ __device__ inline void tile_to_lds(char* lds_tile, const char* gbase, int r0, in
 // row because bit 1 of r becomes bit 2 of the slot).  Padding cannot do both
 // (a 16-byte pad leaves the transposing reads 2-way conflicted).  The pattern
 // repeats every 16 rows.
+//
+// 256-byte rows (d = 128 at 16 bits, 16 chunks) take swz_chunk<16>: bits 0..1
+// of r become bits 2..3 of the slot and bits 2..3 of r bits 0..1, so 16
+// consecutive rows read one chunk in 16 different slots (all banks once) and
+// 4 consecutive rows x 64 bytes fall in 4 different 64-byte quarters.
+template <int C = 8>
 __device__ inline int swz_chunk(int r) {
-  const int p = (r >> 1) & 7;
-  return ((p & 1) << 2) | (p >> 1);
+  static_assert(C == 8 || C == 16, "swizzled rows of 8 or 16 chunks");
+  if constexpr (C == 8) {
+    const int p = (r >> 1) & 7;
+    return ((p & 1) << 2) | (p >> 1);
+  } else {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  }
 }
 
 template <int R, int C, int WAVES, int PAD = 1, bool SWZ = false>
 struct TileLoader {
-  static_assert(!SWZ || (C == 8 && PAD == 0), "swizzled tiles: unpadded 128-byte rows");
+  static_assert(!SWZ || ((C == 8 || C == 16) && PAD == 0), "swizzled tiles: unpadded rows");
   static constexpr int kSlots = R * (C + PAD);
   static constexpr int kInstr = (kSlots + 63) / 64;
   static constexpr int kPer = (kInstr + WAVES - 1) / WAVES;
@@ -315,7 +326,7 @@ struct TileLoader {
       const int row = slot / (C + PAD), c = slot % (C + PAD);
       // the slot's global chunk: the slot's own (swizzled tiles: the chunk
       // stored there), a padding slot a duplicate of chunk 0
-      const int gc = SWZ ? (c ^ swz_chunk(row)) : (c < C ? c : 0);
+      const int gc = SWZ ? (c ^ swz_chunk<SWZ ? C : 8>(row)) : (c < C ? c : 0);
       off[k] = (uint32_t)(row * (C * 16) + gc * 16);
     }
   }
@@ -391,34 +402,38 @@ __device__ inline u32x4 tr_chunk(const char* vtile, int vrow_bytes, int kbase, i
   return r;
 }
 
-// The reads of a swizzled 128-byte-row tile (swz_chunk): offsets fixed per
-// lane, computed once.  row_read: the 16-byte A-operand chunk c (0..3) of row
-// r0 + L % 32, half h, as *(tile + 128 r0 + row[c]) (r0 a multiple of 16).
-// tr_read: what tr_chunk(tile, 128, kbase, ob, ci, lane) reads from an
+// The reads of a swizzled tile of D 16-bit columns (rows of D / 8 chunks,
+// swz_chunk<D / 8>): offsets fixed per lane, computed once.  row_read: the
+// 16-byte A-operand chunk c (0 .. D / 16 - 1) of row r0 + L % 32, half h, as
+// *(tile + RB r0 + row[c]) (RB = 2 D bytes per row, r0 a multiple of 16).
+// tr_read: what tr_chunk(tile, RB, kbase, ob, ci, lane) reads from an
 // unswizzled tile (kbase a multiple of 16).
+template <int D = 64>
 struct SwzReads {
-  uint32_t row[4];
-  uint32_t tr[2][2];
+  static constexpr int C = D / 8;    // chunks per row
+  static constexpr int RB = 2 * D;   // bytes per row
+  uint32_t row[D / 16];
+  uint32_t tr[2][D / 32];
   __device__ inline void init(int lane) {
     const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) row[c] = 128 * l32 + 16 * ((2 * c + h) ^ swz_chunk(l32));
+    for (int c = 0; c < D / 16; ++c) row[c] = RB * l32 + 16 * ((2 * c + h) ^ swz_chunk<C>(l32));
     const int G = lane >> 4, j = lane & 15;
     const int y = 2 * (G & 1) + ((j & 3) >> 1);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int rr = 4 * (G >> 1) + (j >> 2) + 8 * r;
 #pragma unroll
-      for (int ob = 0; ob < 2; ++ob)
-        tr[r][ob] = 128 * rr + 16 * ((4 * ob + y) ^ swz_chunk(rr)) + 8 * (j & 1);
+      for (int ob = 0; ob < D / 32; ++ob)
+        tr[r][ob] = RB * rr + 16 * ((4 * ob + y) ^ swz_chunk<C>(rr)) + 8 * (j & 1);
     }
   }
   __device__ inline u32x4 row_read(const char* tile, int r0, int c) const {
-    return *reinterpret_cast<const u32x4*>(tile + 128 * r0 + row[c]);
+    return *reinterpret_cast<const u32x4*>(tile + RB * r0 + row[c]);
   }
   __device__ inline u32x4 tr_read(const char* tile, int kbase, int ob, int ci) const {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const char* base = tile + 128 * (kbase + 16 * ci);
+    const char* base = tile + RB * (kbase + 16 * ci);
     i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + tr[0][ob]));
     i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + tr[1][ob]));
     u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);

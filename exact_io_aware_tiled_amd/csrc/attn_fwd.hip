@@ -75,8 +75,8 @@ struct FwdCfg {
   // K reads and transposing V reads); at d = 128 rows padded by three 16-byte
   // slots (2 d + 48 bytes: conflict-free K reads, transposing reads 2-way,
   // against 4-way with one slot).  One slot otherwise.
-  static constexpr bool kSwz = kTr && D == 64 && !F8;
-  static constexpr int PAD = kSwz ? 0 : ((kTr && D >= 128 && !F8) ? 3 : 1);
+  static constexpr bool kSwz = kTr && D >= 64 && !F8;
+  static constexpr int PAD = kSwz ? 0 : 1;
   static constexpr int KROW = D * KS + 16 * PAD;  // K tile row stride in LDS (bytes), padded
   // V tile: row-major [BN][DP] (16-bit) or transposed [DP][BN] (float32)
   static constexpr int VROW = F8 == 2 ? 64 + 16 : (kTr ? DP * S + 16 * PAD : BN * S + 16);
@@ -228,7 +228,7 @@ __global__ void
   }
 
   TileLoader<BN, C::CPR, C::kWaves, C::PAD, C::kSwz> tl;
-  SwzReads swz;
+  SwzReads<D> swz;
   if constexpr (C::kSwz) swz.init(lane);
   TileLoader<D, 4, C::kWaves> tlv;  // FP8 values: D rows of 64 codes
   if constexpr (F8 == 2) tlv.init(wave, lane);
