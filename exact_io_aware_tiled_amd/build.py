@@ -19,14 +19,16 @@ LIB = os.path.join(HERE, "libeiat_attn.so")
 SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_decode.hip",
            "attn_fp8.hip"]
 # Machine-scheduler strategy per source, chosen by timing each kernel file's
-# kernels under the strategies LLVM offers for AMDGPU: max-ilp for the forward
-# (its exp/MFMA interleave) and for delta and dK/dV (1-4 % faster than under
-# max-memory-clause).  The dQ kernel, compiled in its own unit, keeps LLVM's
-# default strategy: 1-5 % faster than under max-ilp at n = 4096 causal (d = 64
-# and 128), 1 % slower at d = 128 without mask, n = 16384.
+# kernels under the strategies LLVM offers for AMDGPU (A/B on MI355X, page and
+# training shapes): max-ilp for delta and dK/dV (LLVM's default is 3 % slower
+# at d = 128, max-memory-clause 2 % slower at d = 64) and for dQ (1.3-1.6 %
+# faster than the default at d = 128, equal at d = 64); the forward measures
+# the same under max-ilp and the default (its inner region carries its own
+# scheduling hint) and keeps max-ilp.
 PER_SOURCE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 ARCH = os.environ.get("EIAT_OFFLOAD_ARCH", "gfx950")
 
@@ -114,5 +116,91 @@ def build(verbose: bool = False, extra: list[str] | None = None, checks: bool = 
     return LIB
 
 
+def resource_report(out_path: str) -> str:
+    """Per-kernel register, scratch, LDS and occupancy figures of the product
+    build, from the compiler's resource-usage remarks (a CPU-side compile with
+    -Rpass-analysis=kernel-resource-usage; nothing is linked or run)."""
+    import re
+    import tempfile
+
+    rows = []
+    with tempfile.TemporaryDirectory() as tmp:
+        def one(src):
+            cmd = [HIPCC, *CFLAGS, *PER_SOURCE_FLAGS.get(src, []),
+                   "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+                   "-o", os.path.join(tmp, src + ".o")]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+            return src, r.stderr
+        with cf.ThreadPoolExecutor(max_workers=8) as ex:
+            outs = list(ex.map(one, SOURCES))
+    for src, text in outs:
+        cur = None
+        for line in text.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                cur = {"src": src, "name": m.group(1)}
+                rows.append(cur)
+                continue
+            m = re.search(r"remark:\s+([A-Za-z][A-Za-z \[\]/]*): (\S+) \[", line)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = m.group(2)
+    def short(mangled):
+        # eiat::<kernel><template args>: the kernels' mangled names are all of
+        # the form _ZN4eiat<len><name>I<args>E...
+        m = re.match(r"_ZN4eiat(\d+)", mangled)
+        if not m:
+            return mangled
+        k = int(m.group(1))
+        name = mangled[m.end():m.end() + k]
+        rest = mangled[m.end() + k:]
+        args = []
+        if rest.startswith("I"):
+            body = rest[1:]
+            while body and body[0] != "E":
+                for pat, val in ((r"DF16b", "bf16"), (r"DF16_", "f16"), (r"f", "f32"),
+                                 (r"Lb([01])E", None), (r"Li(-?\d+)E", None)):
+                    mm = re.match(pat, body)
+                    if mm:
+                        args.append(val if val else mm.group(1))
+                        body = body[mm.end():]
+                        break
+                else:
+                    break
+        return f"{name}<{','.join(args)}>"
+
+    lines = [
+        "# Kernel resources of the product build (compiler remarks, gfx950)",
+        "",
+        "command (from the repository root, on any machine with ROCm; compiles, runs nothing):",
+        f"    python exact_io_aware_tiled_amd/build.py --resources {os.path.relpath(out_path, ROOT)}",
+        "",
+        "Per kernel: VGPRs / AGPRs / SGPRs allocated, VGPR and SGPR spills, scratch bytes per",
+        "lane, the occupancy the registers allow (waves per SIMD) and the static LDS per",
+        "workgroup.  LDS also bounds occupancy: 160 KiB per CU, so a 4-wave workgroup of L bytes",
+        "runs floor(163840 / L) workgroups (waves per SIMD) per CU.",
+        "",
+        "Template arguments: element type, d, mask (0 none, 1 causal, 2 window), then",
+        "dropout (0/1) and, for the forward, the FP8 mode (0 none, 1 scores, 2 scores and values).",
+        "",
+        f"{'kernel':<44} {'vgpr':>4} {'agpr':>4} {'sgpr':>4} {'spV':>3} {'spS':>3} "
+        f"{'scr':>4} {'occ':>3} {'lds':>6}",
+    ]
+    for r in rows:
+        d = short(r["name"])
+        lines.append(f"{d:<44} {r.get('VGPRs', '?'):>4} {r.get('AGPRs', '?'):>4} "
+                     f"{r.get('TotalSGPRs', '?'):>4} {r.get('VGPRs Spill', '?'):>3} "
+                     f"{r.get('SGPRs Spill', '?'):>3} {r.get('ScratchSize [bytes/lane]', '?'):>4} "
+                     f"{r.get('Occupancy [waves/SIMD]', '?'):>3} "
+                     f"{r.get('LDS Size [bytes/block]', '?'):>6}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
+
+
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    if len(sys.argv) > 2 and sys.argv[1] == "--resources":
+        print(resource_report(os.path.abspath(sys.argv[2])))
+    else:
+        build(verbose=True, extra=sys.argv[1:])

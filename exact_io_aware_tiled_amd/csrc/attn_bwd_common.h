@@ -1,6 +1,5 @@
 // attn_bwd_common.h -- device helpers shared by the two backward translation
-// units (attn_bwd.hip: delta and dK/dV; attn_bwd_dq.hip: dQ), which are
-// compiled apart so that each can take its own machine-scheduler strategy.
+// units (attn_bwd.hip: delta and dK/dV; attn_bwd_dq.hip: dQ).
 #pragma once
 
 #include <type_traits>

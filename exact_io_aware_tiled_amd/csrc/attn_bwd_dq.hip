@@ -9,8 +9,9 @@
 // block: gamma_ij = p_ij (sum_a G_ia V_ja - delta_i), dQ_i = c sum_j gamma_ij K_j.
 // No atomics: every dQ row is owned by one wave.
 //
-// Compiled in its own translation unit (not with attn_bwd.hip) so that it
-// keeps LLVM's default machine-scheduler strategy.
+// Its own translation unit (apart from attn_bwd.hip, with the helpers both
+// share in attn_bwd_common.h), so the two backward kernels compile in parallel
+// and each can take its own scheduler flags (build.py).
 #include "attn_bwd_common.h"
 #include "attn_internal.h"
 
