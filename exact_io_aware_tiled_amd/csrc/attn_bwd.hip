@@ -69,8 +69,10 @@ struct DkvCfg {
   // reads; float32 keeps transposed copies.
   static constexpr bool kTr = (S == 2);
   // LDS bank conflicts of the Q / dO tiles (and of the resident V rows):
-  // swizzled unpadded rows at 16-bit d = 64, three padding slots at 16-bit
-  // d = 128, one otherwise (as the forward's tiles, attn_fwd.hip).
+  // swizzled unpadded rows at 16-bit d = 64 (as the forward's tiles,
+  // attn_fwd.hip); at 16-bit d = 128, whose registers have no room for the
+  // swizzle's per-lane offsets, rows padded by three 16-byte slots (16-byte
+  // reads conflict-free, transposing reads 2-way); one slot otherwise.
   static constexpr bool kSwz = kTr && D == 64;
   static constexpr int PAD = kSwz ? 0 : ((kTr && D >= 128) ? 3 : 1);
   static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // Q / dO natural rows

@@ -34,8 +34,8 @@ struct DqCfg {
   static constexpr bool kTr = (S == 2);
   static constexpr bool kDirect = kTr && D >= 32;
   // LDS bank conflicts of the K and V tiles: swizzled unpadded rows at 16-bit
-  // d = 64, three padding slots at 16-bit d = 128, one otherwise (as the
-  // forward's tiles, attn_fwd.hip).
+  // d = 64 and 128, one padding slot otherwise (as the forward's tiles,
+  // attn_fwd.hip).
   static constexpr bool kSwz = kDirect && D >= 64;
   static constexpr int PAD = kSwz ? 0 : 1;
   static constexpr int NROW = (kTr ? DP : D) * S + 16 * PAD;  // K, V natural rows

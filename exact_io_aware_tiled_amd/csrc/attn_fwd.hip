@@ -70,11 +70,10 @@ struct FwdCfg {
   static constexpr int S = Elt<T>::kBytes;
   static constexpr bool kTr = (S == 2);       // 16-bit: V row-major + transpose reads
   static constexpr int KS = F8 ? 1 : S;       // bytes per Q / K element (FP8 scores: 1)
-  // LDS bank conflicts of the 16-bit tiles loaded directly: at d = 64,
+  // LDS bank conflicts of the 16-bit tiles loaded directly (d = 64 and 128):
   // unpadded rows with XOR-swizzled chunks (swz_chunk: conflict-free 16-byte
-  // K reads and transposing V reads); at d = 128 rows padded by three 16-byte
-  // slots (2 d + 48 bytes: conflict-free K reads, transposing reads 2-way,
-  // against 4-way with one slot).  One slot otherwise.
+  // K reads and transposing V reads).  Rows padded by one 16-byte slot
+  // otherwise.
   static constexpr bool kSwz = kTr && D >= 64 && !F8;
   static constexpr int PAD = kSwz ? 0 : 1;
   static constexpr int KROW = D * KS + 16 * PAD;  // K tile row stride in LDS (bytes), padded
