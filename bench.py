@@ -8,6 +8,10 @@ per-row delta, then dK/dV; called through attn_bwd_stage so each kernel can be
 timed on its own).  Default workload: batch 1, 32 heads,
 n = 4096, d = v = 64, bf16, causal, c = 1/8.
 
+Timing: --settle-s seconds (default 0.3) of untimed back-to-back steps, so
+that the engine clock has settled under sustained load, then --warmup untimed
+steps, then --steps timed steps (the line's `settle` records the first phase).
+
 Prints ONE JSON line on stdout.  `value` is whole-step algorithmic TFLOP/s with
 the FLOP convention: forward 4 d per allowed (query, key) pair (two products
 of 2 d), backward 2.5 x forward.  `roofline` is for the kernel with the largest
@@ -274,7 +278,7 @@ def bench_fp8(args, w):
     kernels.append((fwd_name, fwd8))
     log(f"bench: fp8 workload {w}")
     K = args.steps
-    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream)
+    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream, args.settle_s)
     log("bench: kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in kern_ms.items()}))
 
     bh = B * H
@@ -308,6 +312,7 @@ def bench_fp8(args, w):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": dict(SETTLE),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -342,10 +347,21 @@ def copy_calibration(torch, dev, mib: int):
     log(f"bench: copy calibration {nbytes} bytes read, {nbytes} bytes written")
 
 
-def time_kernels(torch, kernels, warmup: int, steps: int, stream):
+SETTLE = {"seconds": 0.0, "steps": 0}
+
+
+def time_kernels(torch, kernels, warmup: int, steps: int, stream, settle_s: float = 0.0):
     """Run `steps` timed steps (each: every kernel once, in order) after
     `warmup` untimed ones; per-kernel mean ms from HIP events on `stream`,
-    and the wall-clock ms per step."""
+    and the wall-clock ms per step.
+
+    Before the warmup steps, steps run back to back for `settle_s` seconds
+    (untimed; recorded in SETTLE).  The engine clock takes tens of
+    milliseconds of sustained load to settle: on MI355X the page step ran
+    at 351 us right after start, 385-408 us 10-16 ms in, and 337 us from
+    about 30 ms on.  A few warmup steps of a sub-millisecond step end inside
+    that transient, so without the settle phase the timed steps measure the
+    power management's ramp rather than the kernels' sustained rate."""
     def step(evs=None):
         for i, (_, fn) in enumerate(kernels):
             if evs is not None:
@@ -354,6 +370,14 @@ def time_kernels(torch, kernels, warmup: int, steps: int, stream):
         if evs is not None:
             evs[len(kernels)].record(stream)
 
+    n_settle = 0
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            step()
+        n_settle += 4
+        torch.cuda.synchronize()
+    SETTLE.update(seconds=settle_s, steps=n_settle)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -424,7 +448,7 @@ def bench_decode(args, w):
 
     log(f"bench: decode workload {w}")
     kernels = [("decode_split", stage(0)), ("decode_merge", stage(1))]
-    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, args.steps, stream)
+    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, args.steps, stream, args.settle_s)
     log("bench: kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in kern_ms.items()}))
 
     e = q.element_size()
@@ -451,6 +475,7 @@ def bench_decode(args, w):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": dict(SETTLE),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -477,6 +502,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed back-to-back steps before the warmup steps, so that "
+                         "the engine clock has settled under load (0 disables)")
     ap.add_argument("--workload", default="page_d64")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward alone")
     ap.add_argument("--p-drop", type=float, default=0.0,
@@ -567,7 +595,7 @@ def main():
 
     log(f"bench: workload {w}")
     K = args.steps
-    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream)
+    ms_per_step, kern_ms = time_kernels(torch, kernels, args.warmup, K, stream, args.settle_s)
     log("bench: kernel ms " + json.dumps({k_: round(v_, 4) for k_, v_ in kern_ms.items()}))
 
     bh = B * H
@@ -619,6 +647,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": dict(SETTLE),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -51,8 +51,9 @@ def load_library():
 
 
 def load_check_library(name: str):
-    """One of the check builds (``poison`` or ``alt``, see build.CHECK_BUILDS):
-    the same C ABI compiled with a checking macro, for tests only."""
+    """One of the check builds (``poison``, ``alt`` or ``timing``, see
+    build.CHECK_BUILDS): the same C ABI compiled with a checking macro, for
+    tests and the workgroup timeline only."""
     return _open(os.path.join(HERE, f"libeiat_attn_{name}.so"))
 
 

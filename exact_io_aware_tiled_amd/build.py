@@ -56,10 +56,13 @@ CFLAGS = [
 #   libeiat_attn_poison.so  EIAT_LDS_POISON: every direct HBM -> LDS load
 #                           first fills its destination with NaN
 #   libeiat_attn_alt.so     EIAT_ALT_TILES: other tile shapes
+#   libeiat_attn_timing.so  EIAT_WG_TIMING: per-workgroup start / prologue / end
+#                           stamps of the forward (eiat_wg_times; wg_timeline.py)
 CHECK_BUILDS = {
     "poison": (["-DEIAT_LDS_POISON"],
                ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_decode.hip"]),
     "alt": (["-DEIAT_ALT_TILES"], ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]),
+    "timing": (["-DEIAT_WG_TIMING"], ["attn_fwd.hip"]),
 }
 
 

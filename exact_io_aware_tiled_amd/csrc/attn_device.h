@@ -206,6 +206,9 @@ __device__ inline u32x4 fp8_negate(u32x4 w) {
 //   EIAT_ALT_TILES   other tile shapes (keys per streamed tile, query rows per
 //                    dK/dV tile), for the check that results do not depend on
 //                    the block size beyond rounding.
+//   EIAT_WG_TIMING   the forward records per-workgroup wall-clock stamps and
+//                    hardware positions (attn_fwd.hip, eiat_wg_times), for the
+//                    workgroup timeline of a launch; results are unchanged.
 #ifdef EIAT_ALT_TILES
 constexpr bool kAltTiles = true;
 #else

@@ -47,6 +47,19 @@
 
 namespace eiat {
 
+#ifdef EIAT_WG_TIMING
+// Timing check build: for every workgroup of the forward, the constant-rate
+// wall clock (s_memrealtime) at its start, after its prologue (first score
+// block formed) and at its end, where it ran (the HW_ID register: CU, shader
+// array and engine; XCC_ID: the XCD), and the shader clock counter
+// (s_memtime) at its start and end, whose difference over the wall-clock
+// difference is the engine clock the workgroup ran at.  Read with
+// eiat_wg_times.
+constexpr int kWgTimingMax = 1 << 16;
+constexpr int kWgTimingWords = 6;
+__device__ unsigned long long g_wg_times[kWgTimingWords * kWgTimingMax];
+#endif
+
 // F8: 0 16-bit (or float32) scores; 1 FP8 scores; 2 FP8 scores and FP8 weights
 // and values (V in the tile-major layout of attn_quant_fp8_v).
 template <typename T, int D, int F8 = 0>
@@ -137,6 +150,10 @@ __global__ void
   // Consecutive workgroups take consecutive heads of the same query-tile rank;
   // with masks, the heaviest query tiles (most visible keys) are issued first.
   const int bid = blockIdx.x;
+#ifdef EIAT_WG_TIMING
+  const unsigned long long wg_t0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long wg_c0 = __builtin_amdgcn_s_memtime();
+#endif
   const int bh = bid % bh_count;
   int qt = bid / bh_count;
   if (MASK != 0) qt = num_qtiles - 1 - qt;
@@ -569,6 +586,9 @@ __global__ void
   qk(t_lo, sc[0]);
   advance_ksw();
   __syncthreads();  // K_lo is overwritten by K_lo+2 in the first iteration
+#ifdef EIAT_WG_TIMING
+  const unsigned long long wg_t1 = __builtin_amdgcn_s_memrealtime();
+#endif
 
   // Iteration t: the scores of tile t are exponentiated and multiplied into O
   // while S_{t+1} = K_{t+1} Q^T is formed; V_{t+1} and K_{t+2}, loaded from HBM
@@ -680,6 +700,22 @@ __global__ void
       }
     if (h == 0) LSE[head + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
   }
+#ifdef EIAT_WG_TIMING
+  __syncthreads();
+  if (tid == 0 && bid < kWgTimingMax) {
+    const unsigned long long wg_t2 = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long wg_c2 = __builtin_amdgcn_s_memtime();
+    const unsigned hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID, 32 bits
+    const unsigned xcc_id = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // HW_REG_XCC_ID, 16 bits
+    unsigned long long* rec = g_wg_times + kWgTimingWords * bid;
+    rec[0] = wg_t0;
+    rec[1] = wg_t1;
+    rec[2] = wg_t2;
+    rec[3] = ((unsigned long long)xcc_id << 32) | hw_id;
+    rec[4] = wg_c0;
+    rec[5] = wg_c2;
+  }
+#endif
 }
 
 template <typename T, int D, int MASK, bool DROP, int F8>
@@ -721,6 +757,25 @@ static hipError_t launch_fwd_dt(const FwdArgs& a) {
     default: return launch_fwd_d<T, 128>(a);
   }
 }
+
+#ifdef EIAT_WG_TIMING
+// Copies the stamps of the last forward launch (6 words per workgroup: wall
+// clock at start, after the prologue and at the end, hardware ids, shader
+// clock at start and end; workgroups 0 .. min(grid, 65536) - 1) to host memory
+// `dst` and the wall clock's rate in kHz to *clock_khz.  Returns a hipError_t
+// code.
+extern "C" __attribute__((visibility("default"))) int eiat_wg_times(void* dst, size_t bytes,
+                                                                    int* clock_khz) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(clock_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_wg_times),
+                            bytes < sizeof(g_wg_times) ? bytes : sizeof(g_wg_times), 0,
+                            hipMemcpyDeviceToHost);
+  return (int)e;
+}
+#endif
 
 hipError_t launch_fwd(const FwdArgs& a) {
   switch (a.dtype) {

@@ -6,6 +6,10 @@ with NaN.  A kernel that read a tile before its loads had landed and been
 published by a barrier would return non-finite or different values; a
 correctly synchronized one returns bitwise the results of the product build.
 
+Timing build: the forward also records per-workgroup wall-clock stamps and
+hardware positions (wg_timeline.py reads them); its outputs must be bitwise the
+product's, and the stamps must be complete and ordered.
+
 Tile-shape build: other keys-per-tile and rows-per-tile.  The exactness theorem
 (alphabetamath.cc, Theorem "Tiled attention and its recomputed reverse pass are
 exact") makes the result independent of the block size; in floating point
@@ -128,3 +132,30 @@ def test_other_tile_shapes_agree(w):
         gq, gk, gv, _, _, _ = oracle.bwd(q, k, v, do, w.c, w.mask, w.window)
         for g, r, nm in zip(got[2:], (gq, gk, gv), ("dQ", "dK", "dV")):
             check_grad(to64(g), r, g.dtype, f"alt tiles {nm}")
+
+
+@pytest.mark.parametrize("w", [WORKLOADS["page_d64"].replace(H=8),
+                               Workload("small", 2, 3, 333, 128, 128, "bf16", "causal", seed=83),
+                               Workload("small", 1, 2, 300, 64, 64, "f16", "window", window=70,
+                                        seed=89)],
+                         ids=lambda w: f"{w.name}-{w.d}-{w.mask}-{w.n}")
+def test_timing_build(w):
+    inp = make_inputs(w, with_grad=True)
+    ref = fwd_bwd(A.load_library(), w, inp)
+    lib = A.load_check_library("timing")
+    lib.eiat_wg_times.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
+    lib.eiat_wg_times.restype = ctypes.c_int
+    got = fwd_bwd(lib, w, inp)
+    for name, a, b in zip(("O", "LSE"), got, ref):
+        assert torch.equal(a, b), name
+    grid = w.B * w.H * ((w.n + 127) // 128)
+    buf = np.zeros(6 * grid, np.uint64)
+    khz = ctypes.c_int(0)
+    assert lib.eiat_wg_times(buf.ctypes.data, buf.nbytes, ctypes.byref(khz)) == 0
+    assert khz.value > 0
+    r = buf.reshape(grid, 6).astype(np.int64)
+    assert (r[:, 0] > 0).all(), "a workgroup left no stamp"
+    assert (r[:, 0] <= r[:, 1]).all() and (r[:, 1] <= r[:, 2]).all()
+    span_us = (r[:, 2].max() - r[:, 0].min()) * 1e3 / khz.value
+    assert 0 < span_us < 1e6
+    assert (r[:, 5] >= r[:, 4]).all()  # shader clock counter, start to end
