@@ -263,125 +263,149 @@ __global__ void __launch_bounds__(256)
       const char* b = smem + buf * C::BUF;
 
       // One tile, with the per-element mask compiled in or out, so that the
-      // unmasked body has no branch and the scheduler can overlap the 32-row
-      // blocks (the next block's LDS reads and MFMAs with this one's exponentials).
-      auto tile_body = [&](auto masked) __attribute__((always_inline)) {
-  #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          // scheduling hint: interleave LDS operand reads with the MFMAs
-          __builtin_amdgcn_iglp_opt(0);
-          // S = Q K^T and dP - delta = dO V^T - delta for 32 query rows x this
-          // wave's 32 keys (without dropout the dP accumulator starts at -delta of
-          // its row, so dS = p (dP - delta) needs no subtraction afterwards)
-          const float* ls = reinterpret_cast<const float*>(b + C::LS);
-          const float* dl = reinterpret_cast<const float*>(b + C::DL);  // -delta
-          f32x16 s, dp;
-  #pragma unroll
-          for (int e = 0; e < 16; ++e) s[e] = 0.0f;
-          if constexpr (DROP) {
-  #pragma unroll
-            for (int e = 0; e < 16; ++e) dp[e] = 0.0f;
-          } else {
-  #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
-              dp[4 * g] = d4.x;
-              dp[4 * g + 1] = d4.y;
-              dp[4 * g + 2] = d4.z;
-              dp[4 * g + 3] = d4.w;
-            }
-          }
-          const int rq = 32 * qb + l32;
-  #pragma unroll
-          for (int c = 0; c < C::NCH; ++c) {
-            u32x4 qa, oa;
-            if constexpr (C::kSwz) {
-              qa = swz.row_read(b + C::QN, 32 * qb, c);
-              oa = swz.row_read(b + C::ON, 32 * qb, c);
-            } else {
-              qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
-              oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
-            }
-            s = Elt<T>::mma(qa, kf[c], s);
-            u32x4 vb4;
-            if constexpr (C::kVLds)
-              vb4 = *reinterpret_cast<const u32x4*>(smem + C::VRES + (32 * wave + l32) * C::NROW +
-                                                    32 * c + 16 * h);
-            else
-              vb4 = vf[c];
-            dp = Elt<T>::mma(oa, vb4, dp);
-          }
-          if (mask_on(masked)) {
-  #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int q = qt0 + 32 * qb + 8 * (e >> 2) + 4 * h + (e & 3);
-              if (!key_allowed<MASK>(q, key, n, window)) s[e] = -INFINITY;
-            }
-          }
-          // p = 2^(s c log2 e - LSE log2 e), dS = p (dP - delta)
-  #pragma unroll
+      // unmasked body has no branch.  At 16-bit d = 64 it is software-pipelined
+      // over the 32-row blocks: the score and dP products of block qb + 1 are
+      // issued before the exponentials of block qb, so that they run under them.
+      const float* ls = reinterpret_cast<const float*>(b + C::LS);
+      const float* dl = reinterpret_cast<const float*>(b + C::DL);  // -delta
+      // S = Q K^T and dP - delta = dO V^T - delta for 32 query rows x this
+      // wave's 32 keys (without dropout the dP accumulator starts at -delta of
+      // its row, so dS = p (dP - delta) needs no subtraction afterwards)
+      auto sdp = [&](int qb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+        if constexpr (DROP) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) dp[e] = 0.0f;
+        } else {
+#pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const float4 l4 = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * g + 4 * h);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            float ndl[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // -delta (dropout path only)
+            const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
+            dp[4 * g] = d4.x;
+            dp[4 * g + 1] = d4.y;
+            dp[4 * g + 2] = d4.z;
+            dp[4 * g + 3] = d4.w;
+          }
+        }
+        const int rq = 32 * qb + l32;
+#pragma unroll
+        for (int c = 0; c < C::NCH; ++c) {
+          u32x4 qa, oa;
+          if constexpr (C::kSwz) {
+            qa = swz.row_read(b + C::QN, 32 * qb, c);
+            oa = swz.row_read(b + C::ON, 32 * qb, c);
+          } else {
+            qa = *reinterpret_cast<const u32x4*>(b + C::QN + rq * C::NROW + 32 * c + 16 * h);
+            oa = *reinterpret_cast<const u32x4*>(b + C::ON + rq * C::NROW + 32 * c + 16 * h);
+          }
+          s = Elt<T>::mma(qa, kf[c], s);
+          u32x4 vb4;
+          if constexpr (C::kVLds)
+            vb4 = *reinterpret_cast<const u32x4*>(smem + C::VRES + (32 * wave + l32) * C::NROW +
+                                                  32 * c + 16 * h);
+          else
+            vb4 = vf[c];
+          dp = Elt<T>::mma(oa, vb4, dp);
+        }
+      };
+      auto rest = [&](int qb, f32x16& s, f32x16& dp, auto masked) __attribute__((always_inline)) {
+        if (mask_on(masked)) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int q = qt0 + 32 * qb + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (!key_allowed<MASK>(q, key, n, window)) s[e] = -INFINITY;
+          }
+        }
+        // p = 2^(s c log2 e - LSE log2 e), dS = p (dP - delta)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 l4 = *reinterpret_cast<const float4*>(ls + 32 * qb + 8 * g + 4 * h);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          float ndl[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // -delta (dropout path only)
+          if constexpr (DROP) {
+            const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
+            ndl[0] = d4.x;
+            ndl[1] = d4.y;
+            ndl[2] = d4.z;
+            ndl[3] = d4.w;
+          }
+          // Dropout (DROP): the four rows 32 qb + 8 g + 4 h + i against this
+          // lane's key.  Lane t of each group of four lanes (keys 4m .. 4m + 3)
+          // forms the keep bytes of row i = t for the four keys; a quad
+          // broadcast hands every lane byte (key & 3) of each row's word.
+          uint32_t kb[4] = {0u, 0u, 0u, 0u};
+          if constexpr (DROP) {
+            const int t = l32 & 3;
+            const uint32_t rk = reinterpret_cast<const uint32_t*>(b + C::RK)[32 * qb + 8 * g + 4 * h + t];
+            const uint32_t mine = drop_group_bytes(rk, (uint32_t)key >> 2);
+            kb[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
+            kb[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
+            kb[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
+            kb[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * g + i;
+            const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lv[i]));
             if constexpr (DROP) {
-              const float4 d4 = *reinterpret_cast<const float4*>(dl + 32 * qb + 8 * g + 4 * h);
-              ndl[0] = d4.x;
-              ndl[1] = d4.y;
-              ndl[2] = d4.z;
-              ndl[3] = d4.w;
-            }
-            // Dropout (DROP): the four rows 32 qb + 8 g + 4 h + i against this
-            // lane's key.  Lane t of each group of four lanes (keys 4m .. 4m + 3)
-            // forms the keep bytes of row i = t for the four keys; a quad
-            // broadcast hands every lane byte (key & 3) of each row's word.
-            uint32_t kb[4] = {0u, 0u, 0u, 0u};
-            if constexpr (DROP) {
-              const int t = l32 & 3;
-              const uint32_t rk = reinterpret_cast<const uint32_t*>(b + C::RK)[32 * qb + 8 * g + 4 * h + t];
-              const uint32_t mine = drop_group_bytes(rk, (uint32_t)key >> 2);
-              kb[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
-              kb[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
-              kb[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
-              kb[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
-            }
-  #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int e = 4 * g + i;
-              const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lv[i]));
-              if constexpr (DROP) {
-                const bool keep = drop_keep(kb[i], key & 3, dpar.thr);
-                s[e] = keep ? p : 0.0f;
-                dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) + ndl[i]);
-              } else {
-                s[e] = p;
-                dp[e] = p * dp[e];
-              }
+              const bool keep = drop_keep(kb[i], key & 3, dpar.thr);
+              s[e] = keep ? p : 0.0f;
+              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) + ndl[i]);
+            } else {
+              s[e] = p;
+              dp[e] = p * dp[e];
             }
           }
-          PChunks<T> pc, dsc;
-          pc.set(s);
-          dsc.set(dp);
-  #pragma unroll
-          for (int ob = 0; ob < C::NOB; ++ob) {
-  #pragma unroll
-            for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
-              u32x4 oa, qa2;
-              if constexpr (C::kTr) {
-                if constexpr (C::kSwz) {
-                  oa = swz.tr_read(b + C::ON, 32 * qb, ob, ci);
-                  qa2 = swz.tr_read(b + C::QN, 32 * qb, ob, ci);
-                } else {
-                  oa = tr_chunk(b + C::ON, C::NROW, 32 * qb, ob, ci, lane);
-                  qa2 = tr_chunk(b + C::QN, C::NROW, 32 * qb, ob, ci, lane);
-                }
+        }
+        PChunks<T> pc, dsc;
+        pc.set(s);
+        dsc.set(dp);
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) {
+#pragma unroll
+          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+            u32x4 oa, qa2;
+            if constexpr (C::kTr) {
+              if constexpr (C::kSwz) {
+                oa = swz.tr_read(b + C::ON, 32 * qb, ob, ci);
+                qa2 = swz.tr_read(b + C::QN, 32 * qb, ob, ci);
               } else {
-                oa = keyrow_chunk<T>(b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
-                qa2 = keyrow_chunk<T>(b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
+                oa = tr_chunk(b + C::ON, C::NROW, 32 * qb, ob, ci, lane);
+                qa2 = tr_chunk(b + C::QN, C::NROW, 32 * qb, ob, ci, lane);
               }
-              dv[ob] = Elt<T>::mma(oa, pc.c[ci], dv[ob]);
-              dk[ob] = Elt<T>::mma(qa2, dsc.c[ci], dk[ob]);
+            } else {
+              oa = keyrow_chunk<T>(b + C::OT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
+              qa2 = keyrow_chunk<T>(b + C::QT + (32 * ob + l32) * C::TROW + 32 * qb * C::S, ci, h);
             }
+            dv[ob] = Elt<T>::mma(oa, pc.c[ci], dv[ob]);
+            dk[ob] = Elt<T>::mma(qa2, dsc.c[ci], dk[ob]);
+          }
+        }
+      };
+      // The pipelined order holds two blocks' scores at once (32 more
+      // registers): used where they are free, at 16-bit d = 64 (1 % faster);
+      // d = 16 would drop from three waves per SIMD to two, float32 d = 64
+      // spills, and d = 128 has one block per tile.
+      constexpr bool kPipe = C::kTr && D == 64 && C::NQB > 1;
+      auto tile_body = [&](auto masked) __attribute__((always_inline)) {
+        if constexpr (kPipe) {
+          f32x16 s[2], dp[2];
+          sdp(0, s[0], dp[0]);
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            // scheduling hint: interleave LDS operand reads with the MFMAs
+            __builtin_amdgcn_iglp_opt(0);
+            if (qb + 1 < C::NQB) sdp(qb + 1, s[(qb + 1) & 1], dp[(qb + 1) & 1]);
+            rest(qb, s[qb & 1], dp[qb & 1], masked);
+          }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            // scheduling hint: interleave LDS operand reads with the MFMAs
+            __builtin_amdgcn_iglp_opt(0);
+            f32x16 s, dp;
+            sdp(qb, s, dp);
+            rest(qb, s, dp, masked);
           }
         }
       };
