@@ -28,6 +28,9 @@ struct DqCfg {
   static constexpr int S = Elt<T>::kBytes;
   // keys per streamed tile (the tile-shape check build: 32 for 16-bit types)
   static constexpr int BN = ((S == 4 && D >= 128) || (S == 2 && kAltTiles)) ? 32 : 64;
+  // d = 16 runs three waves per SIMD (the float32 kernels sat two registers
+  // above the three-wave budget otherwise).
+  static constexpr int kMinWaves = D == 16 ? 3 : 1;
   static constexpr int DP = D < 32 ? 32 : D;
   // 16-bit: the K^T operand comes from the natural K tile through transpose
   // reads; float32 keeps a transposed copy.
@@ -50,7 +53,8 @@ struct DqCfg {
 };
 
 template <typename T, int D, int MASK, bool DROP>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(DqCfg<T, D>::kMinWaves, 8))) attn_bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ O, const float* __restrict__ LSE,
     float* __restrict__ delta, T* __restrict__ dQ, int n, int bh_count, int num_qtiles,
@@ -170,75 +174,98 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(
       bool straddle = j0 + BN > n;
       if (MASK != 0) straddle = straddle || (j0 + BN - 1 > qw0);
       if (MASK == 2) straddle = straddle || (j0 < qw0 + 31 - window + 1);
+      // S^T = K Q^T and dP^T = V dO^T for key block sb: lane holds one query
+      // row, 16 keys per half (without dropout dP^T starts at -delta of the
+      // lane's row, so dS = p (dP - delta) needs no subtraction afterwards)
+      auto sdp = [&](int sb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
-        // scheduling hint: interleave LDS operand reads with the MFMAs
-        __builtin_amdgcn_iglp_opt(0);
-        // S^T = K Q^T and dP^T = V dO^T: lane holds one query row, 16 keys per half
-        // (without dropout dP^T starts at -delta of the lane's row, so
-        // dS = p (dP - delta) needs no subtraction afterwards)
-        f32x16 s, dp;
+      for (int e = 0; e < 16; ++e) {
+        s[e] = 0.0f;
+        dp[e] = DROP ? 0.0f : -dlt;
+      }
+      const int rk = 32 * sb + l32;
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c) {
+        u32x4 ka, va;
+        if constexpr (C::kSwz) {
+          ka = swz.row_read(b + C::KN, 32 * sb, c);
+          va = swz.row_read(b + C::VN, 32 * sb, c);
+        } else {
+          ka = *reinterpret_cast<const u32x4*>(b + C::KN + rk * C::NROW + 32 * c + 16 * h);
+          va = *reinterpret_cast<const u32x4*>(b + C::VN + rk * C::NROW + 32 * c + 16 * h);
+        }
+        s = Elt<T>::mma(ka, qf[c], s);
+        dp = Elt<T>::mma(va, of[c], dp);
+      }
+      };
+      // mask, P, dS = P (dP - delta), dQ^T += K^T dS^T for key block sb
+      auto rest = [&](int sb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+      if (straddle) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          s[e] = 0.0f;
-          dp[e] = DROP ? 0.0f : -dlt;
+          const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (!key_allowed<MASK>(qrow, j, n, window)) s[e] = -INFINITY;
         }
-        const int rk = 32 * sb + l32;
+      }
+      if constexpr (DROP) {
+        const int jb = j0 + 32 * sb + 4 * h;  // key of element e = 0
 #pragma unroll
-        for (int c = 0; c < C::NCH; ++c) {
-          u32x4 ka, va;
-          if constexpr (C::kSwz) {
-            ka = swz.row_read(b + C::KN, 32 * sb, c);
-            va = swz.row_read(b + C::VN, 32 * sb, c);
-          } else {
-            ka = *reinterpret_cast<const u32x4*>(b + C::KN + rk * C::NROW + 32 * c + 16 * h);
-            va = *reinterpret_cast<const u32x4*>(b + C::VN + rk * C::NROW + 32 * c + 16 * h);
-          }
-          s = Elt<T>::mma(ka, qf[c], s);
-          dp = Elt<T>::mma(va, of[c], dp);
-        }
-        if (straddle) {
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t bytes = drop_group_bytes(row_key, (uint32_t)(jb + 8 * k) >> 2);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int j = j0 + 32 * sb + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (!key_allowed<MASK>(qrow, j, n, window)) s[e] = -INFINITY;
-          }
-        }
-        if constexpr (DROP) {
-          const int jb = j0 + 32 * sb + 4 * h;  // key of element e = 0
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t bytes = drop_group_bytes(row_key, (uint32_t)(jb + 8 * k) >> 2);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int e = 4 * k + r;
-              const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
-              const bool keep = drop_keep(bytes, r, dpar.thr);
-              dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) - dlt);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * k + r;
             const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
-            dp[e] = p * dp[e];
+            const bool keep = drop_keep(bytes, r, dpar.thr);
+            dp[e] = p * ((keep ? dp[e] * dpar.inv_keep : 0.0f) - dlt);
           }
         }
-        PChunks<T> dsc;
-        dsc.set(dp);
+      } else {
 #pragma unroll
-        for (int ob = 0; ob < C::NOB; ++ob) {
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[e], qk_scale, -lse2));
+          dp[e] = p * dp[e];
+        }
+      }
+      PChunks<T> dsc;
+      dsc.set(dp);
 #pragma unroll
-          for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
-            u32x4 ka2;
-            if constexpr (C::kSwz)
-              ka2 = swz.tr_read(b + C::KN, 32 * sb, ob, ci);
-            else if constexpr (C::kTr)
-              ka2 = tr_chunk(b + C::KN, C::NROW, 32 * sb, ob, ci, lane);
-            else
-              ka2 = keyrow_chunk<T>(b + C::KT + (32 * ob + l32) * C::TROW + 32 * sb * C::S, ci, h);
-            dq[ob] = Elt<T>::mma(ka2, dsc.c[ci], dq[ob]);
-          }
+      for (int ob = 0; ob < C::NOB; ++ob) {
+#pragma unroll
+        for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+          u32x4 ka2;
+          if constexpr (C::kSwz)
+            ka2 = swz.tr_read(b + C::KN, 32 * sb, ob, ci);
+          else if constexpr (C::kTr)
+            ka2 = tr_chunk(b + C::KN, C::NROW, 32 * sb, ob, ci, lane);
+          else
+            ka2 = keyrow_chunk<T>(b + C::KT + (32 * ob + l32) * C::TROW + 32 * sb * C::S, ci, h);
+          dq[ob] = Elt<T>::mma(ka2, dsc.c[ci], dq[ob]);
+        }
+      }
+      };
+      // At 16-bit d = 128 the block loop is software-pipelined: the S and dP
+      // products of block sb + 1 are issued before the exponentials of block
+      // sb (1-2 % faster; the 16 extra registers fit the two waves per SIMD).
+      // At d = 64 they would cost the third wave (4 % slower).
+      if constexpr (C::kTr && D == 128 && C::NSB > 1) {
+        f32x16 s[2], dp[2];
+        sdp(0, s[0], dp[0]);
+#pragma unroll
+        for (int sb = 0; sb < C::NSB; ++sb) {
+          // scheduling hint: interleave LDS operand reads with the MFMAs
+          __builtin_amdgcn_iglp_opt(0);
+          if (sb + 1 < C::NSB) sdp(sb + 1, s[(sb + 1) & 1], dp[(sb + 1) & 1]);
+          rest(sb, s[sb & 1], dp[sb & 1]);
+        }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < C::NSB; ++sb) {
+          // scheduling hint: interleave LDS operand reads with the MFMAs
+          __builtin_amdgcn_iglp_opt(0);
+          f32x16 s, dp;
+          sdp(sb, s, dp);
+          rest(sb, s, dp);
         }
       }
     }
