@@ -85,11 +85,13 @@ struct FwdCfg {
   static constexpr int KS = F8 ? 1 : S;       // bytes per Q / K element (FP8 scores: 1)
   // LDS bank conflicts of the 16-bit tiles loaded directly (d = 64 and 128):
   // unpadded rows with XOR-swizzled chunks (swz_chunk: conflict-free 16-byte
-  // K reads and transposing V reads).  Rows padded by one 16-byte slot
-  // otherwise.
-  static constexpr bool kSwz = kTr && D >= 64 && !F8;
-  static constexpr int PAD = kSwz ? 0 : 1;
-  static constexpr int KROW = D * KS + 16 * PAD;  // K tile row stride in LDS (bytes), padded
+  // K reads and transposing V reads).  With FP8 scores the 16-bit V tiles at
+  // d = 128 are swizzled too (3-8 % faster; at d = 64 1 % slower) and the FP8
+  // K rows keep one padding slot.  Rows padded by one 16-byte slot otherwise.
+  static constexpr bool kSwz = kTr && D >= 64 && (F8 == 0 || (F8 == 1 && D == 128));
+  static constexpr int PAD = kSwz ? 0 : 1;                   // V rows (and 16-bit K rows)
+  static constexpr int KPAD = (kSwz && !F8) ? 0 : 1;         // K rows
+  static constexpr int KROW = D * KS + 16 * KPAD;  // K tile row stride in LDS (bytes), padded
   // V tile: row-major [BN][DP] (16-bit) or transposed [DP][BN] (float32)
   static constexpr int VROW = F8 == 2 ? 64 + 16 : (kTr ? DP * S + 16 * PAD : BN * S + 16);
   static constexpr int KBYTES = BN * KROW;
