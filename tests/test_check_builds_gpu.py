@@ -159,3 +159,16 @@ def test_timing_build(w):
     span_us = (r[:, 2].max() - r[:, 0].min()) * 1e3 / khz.value
     assert 0 < span_us < 1e6
     assert (r[:, 5] >= r[:, 4]).all()  # shader clock counter, start to end
+
+
+def test_wg_timeline_summary():
+    """The workgroup-timeline summary runs end to end on a small workload."""
+    from exact_io_aware_tiled_amd import wg_timeline
+
+    lib = A.load_check_library("timing")
+    lib.eiat_wg_times.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
+    lib.eiat_wg_times.restype = ctypes.c_int
+    announce("wg_timeline smoke")
+    out = wg_timeline.timeline(lib, "smoke", warm_s=0.05)
+    for key in ("span", "slot use", "prologue", "steady rate", "clock"):
+        assert key in out, out
