@@ -244,11 +244,6 @@ __global__ void __launch_bounds__(256)
         }
       }
       };
-      // At 16-bit d >= 64 the block loop is software-pipelined: the S and dP
-      // products of block sb + 1 are issued before the exponentials of block
-      // sb.  At d = 128 the extra registers fit the two waves per SIMD (1-2 %
-      // faster); at d = 64 they cost the third wave, which without the raised
-      // priority below measured 4 % slower and with it 2-4 % faster.
       // Raised wave priority over the exponentials and dQ products of a block
       // (16-bit d >= 64), so that they go ahead of the other wave's score
       // products: 6.5 % faster at d = 128 with the pipelined loop; at d = 16
@@ -259,6 +254,11 @@ __global__ void __launch_bounds__(256)
         rest(sb, s, dp);
         if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
       };
+      // At 16-bit d >= 64 the block loop is software-pipelined: the S and dP
+      // products of block sb + 1 are issued before the exponentials of block
+      // sb.  At d = 128 the extra registers fit the two waves per SIMD (1-2 %
+      // faster); at d = 64 they cost the third wave, which without the raised
+      // priority above measured 4 % slower and with it 2-4 % faster.
       if constexpr (C::kTr && D >= 64 && C::NSB > 1) {
         f32x16 s[2], dp[2];
         sdp(0, s[0], dp[0]);
