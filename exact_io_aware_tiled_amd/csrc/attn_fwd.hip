@@ -354,11 +354,10 @@ __global__ void
     }
   };
 
-  // S^T block of tile t = K_t Q_w^T (fp32 accumulate)
-  auto qk = [&](int t, f32x16 (&s)[C::NSB]) __attribute__((always_inline)) {
+  // 32-key block sb of the S^T block of tile t = K_t Q_w^T (fp32 accumulate)
+  auto qk_block = [&](int t, f32x16 (&s)[C::NSB], int sb) __attribute__((always_inline)) {
     const char* kb = kbuf(t);
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
+    {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[sb][e] = 0.0f;
       if constexpr (F8) {
@@ -382,6 +381,10 @@ __global__ void
         }
       }
     }
+  };
+  auto qk = [&](int t, f32x16 (&s)[C::NSB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) qk_block(t, s, sb);
   };
 
   // Running summary of this lane's query row.  Both half-waves keep the same
@@ -470,9 +473,52 @@ __global__ void
     // A row with no allowed key so far keeps the empty summary: shift by 0.
     return (m_run == -INFINITY) ? 0.0f : m_run;
   };
-  auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use, auto masked) __attribute__((always_inline)) {
+  // One 32-key block of exp_pv_tile (every mode but FP8 values).
+  auto exp_pv_block = [&](int t, f32x16 (&s)[C::NSB], float m_use, auto masked, int sb)
+      __attribute__((always_inline)) {
     const char* vb = vbuf(t);
+    if (!active(sb, masked)) return;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
+    PChunks<T> pc;
+    if constexpr (DROP) {
+      // l sums the undropped weights; then dropped weights become 0 in the
+      // value product (the kept ones are scaled by 256 / (256 - thr) at the end).
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ps[e & 3] += s[sb][e];
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      const int jb = t * BN + 32 * sb + 4 * h;  // key of element e = 0
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t bytes = drop_group_bytes(row_key, (uint32_t)(jb + 8 * k) >> 2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!drop_keep(bytes, r, dp.thr)) s[sb][4 * k + r] = 0.0f;
+      }
+      pc.set(s[sb]);
+    } else {
+      pc.set(s[sb]);
+      l_run = chunk_sum<T>(pc, s[sb], l_run);
+    }
+#pragma unroll
+    for (int ob = 0; ob < C::NOB; ++ob) {
+#pragma unroll
+      for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
+        u32x4 va;
+        if constexpr (C::kSwz)
+          va = swz.tr_read(vb, 32 * sb, ob, ci);
+        else if constexpr (C::kTr)
+          va = tr_chunk(vb, C::VROW, 32 * sb, ob, ci, lane);
+        else
+          va = keyrow_chunk<T>(vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S, ci, h);
+        o[ob] = Elt<T>::mma(va, pc.c[ci], o[ob]);
+      }
+    }
+  };
+  auto exp_pv_tile = [&](int t, f32x16 (&s)[C::NSB], float m_use, auto masked) __attribute__((always_inline)) {
     if constexpr (F8 == 2) {
+      const char* vb = vbuf(t);
       // FP8 weights: P rounded to e4m3 with a unit scale (P <= 2^8 < 448),
       // the lane's 16 keys of each 32-key block in accumulator order, which is
       // the byte order of the V^T codes; one block-scaled MFMA per 64 keys and
@@ -506,46 +552,7 @@ __global__ void
       return;
     }
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      if (!active(sb, masked)) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[sb][e] = fast_exp2(__builtin_fmaf(s[sb][e], qk_scale, -m_use));
-      PChunks<T> pc;
-      if constexpr (DROP) {
-        // l sums the undropped weights; then dropped weights become 0 in the
-        // value product (the kept ones are scaled by 256 / (256 - thr) at the end).
-        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ps[e & 3] += s[sb][e];
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        const int jb = t * BN + 32 * sb + 4 * h;  // key of element e = 0
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t bytes = drop_group_bytes(row_key, (uint32_t)(jb + 8 * k) >> 2);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (!drop_keep(bytes, r, dp.thr)) s[sb][4 * k + r] = 0.0f;
-        }
-        pc.set(s[sb]);
-      } else {
-        pc.set(s[sb]);
-        l_run = chunk_sum<T>(pc, s[sb], l_run);
-      }
-#pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob) {
-#pragma unroll
-        for (int ci = 0; ci < PChunks<T>::kCount; ++ci) {
-          u32x4 va;
-          if constexpr (C::kSwz)
-            va = swz.tr_read(vb, 32 * sb, ob, ci);
-          else if constexpr (C::kTr)
-            va = tr_chunk(vb, C::VROW, 32 * sb, ob, ci, lane);
-          else
-            va = keyrow_chunk<T>(vb + (32 * ob + l32) * C::VROW + 32 * sb * C::S, ci, h);
-          o[ob] = Elt<T>::mma(va, pc.c[ci], o[ob]);
-        }
-      }
-    }
+    for (int sb = 0; sb < C::NSB; ++sb) exp_pv_block(t, s, m_use, masked, sb);
   };
 
   // Prologue: K_lo, V_lo and K_lo+1 in LDS, S_lo in registers.
@@ -627,6 +634,16 @@ __global__ void
     if constexpr (C::kDoubleS) {
       next_scores(nxt);
       exp_pv_tile(t, cur, m_use, masked);
+    } else if constexpr (!decltype(masked)::value && F8 == 0) {
+      // One score buffer, mask-free body: block sb of the next tile's scores
+      // right after block sb's value products (its scores are consumed by
+      // then), so that the score products are spread over the exponentials of
+      // the later blocks (1-2 % faster at d = 64, bitwise unchanged).
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        exp_pv_block(t, cur, m_use, masked, sb);
+        qk_block(t + 1, nxt, sb);
+      }
     } else {
       exp_pv_tile(t, cur, m_use, masked);
       next_scores(nxt);
