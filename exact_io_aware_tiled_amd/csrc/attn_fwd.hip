@@ -634,11 +634,12 @@ __global__ void
     if constexpr (C::kDoubleS) {
       next_scores(nxt);
       exp_pv_tile(t, cur, m_use, masked);
-    } else if constexpr (!decltype(masked)::value && F8 == 0) {
+    } else if constexpr (!decltype(masked)::value && F8 == 0 && !DROP) {
       // One score buffer, mask-free body: block sb of the next tile's scores
       // right after block sb's value products (its scores are consumed by
       // then), so that the score products are spread over the exponentials of
-      // the later blocks (1-2 % faster at d = 64, bitwise unchanged).
+      // the later blocks (1-2 % faster at d = 64, bitwise unchanged; with
+      // dropout 10 % slower, so left out there).
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) {
         exp_pv_block(t, cur, m_use, masked, sb);
