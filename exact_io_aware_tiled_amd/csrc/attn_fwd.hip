@@ -631,20 +631,29 @@ __global__ void
         qk(t + 1, s);
       }
     };
-    if constexpr (C::kDoubleS) {
-      next_scores(nxt);
-      exp_pv_tile(t, cur, m_use, masked);
-    } else if constexpr (!decltype(masked)::value && F8 == 0 && !DROP) {
-      // One score buffer, mask-free body: block sb of the next tile's scores
-      // right after block sb's value products (its scores are consumed by
-      // then), so that the score products are spread over the exponentials of
-      // the later blocks (1-2 % faster at d = 64, bitwise unchanged; with
-      // dropout 10 % slower, so left out there).
+    // In the mask-free 16-bit body the two products are issued block by block,
+    // so that the compiler spreads the score products over the exponentials
+    // (bitwise unchanged; with dropout 10 % slower at d = 64, so left out
+    // there).  One score buffer: block sb of the next tile's scores right after
+    // block sb's value products, whose scores are consumed by then (1-2 %
+    // faster at d = 64).  Two buffers: block sb of the next tile's scores, then
+    // block sb's exponentials and value products (0.5-1 % faster at d = 128).
+    constexpr bool kBlockwise = !decltype(masked)::value && F8 == 0 && !DROP;
+    if constexpr (kBlockwise && C::kDoubleS) {
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        qk_block(t + 1, nxt, sb);
+        exp_pv_block(t, cur, m_use, masked, sb);
+      }
+    } else if constexpr (kBlockwise) {
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) {
         exp_pv_block(t, cur, m_use, masked, sb);
         qk_block(t + 1, nxt, sb);
       }
+    } else if constexpr (C::kDoubleS) {
+      next_scores(nxt);
+      exp_pv_tile(t, cur, m_use, masked);
     } else {
       exp_pv_tile(t, cur, m_use, masked);
       next_scores(nxt);
