@@ -602,10 +602,10 @@ __global__ void
   // Iteration t: the scores of tile t are exponentiated and multiplied into O
   // while S_{t+1} = K_{t+1} Q^T is formed; V_{t+1} and K_{t+2}, loaded from HBM
   // at the top, are stored for the next iteration.  With one score buffer
-  // S_{t+1} overwrites S_t after its exponentials (the scheduler interleaves
-  // those MFMAs with the second half of the tile); with two (d = 128, twice
-  // the MFMA work per tile) S_{t+1} is issued first into the other buffer.
-  // cur holds S_t; nxt receives S_{t+1} (the same buffer below d = 128).
+  // S_{t+1} overwrites S_t block by block after its exponentials; with two
+  // (d = 128, twice the MFMA work per tile) each block of S_{t+1} goes into
+  // the other buffer ahead of the same block of S_t's exponentials.  cur holds
+  // S_t; nxt receives S_{t+1} (the same buffer below d = 128).
   auto iterate = [&](int t, f32x16 (&cur)[C::NSB], f32x16 (&nxt)[C::NSB], auto masked)
       __attribute__((always_inline)) {
     const bool has1 = t + 1 < t_hi, has2 = t + 2 < t_hi;
