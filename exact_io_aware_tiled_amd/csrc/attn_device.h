@@ -454,11 +454,15 @@ __device__ inline float wave_other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
-// max / sum over the two half-waves (symmetric, so either result order works)
+// max / sum over the two half-waves (symmetric, so either result order works).
+// The row maxima use IEEE maximum (v_maximum3_f32), which needs no quieting
+// of its operands first, where fmaxf costs a v_max_f32 per operand that the
+// compiler cannot prove canonical (the permlane results, the first score).
+// Scores are finite or -inf, for which the two agree; a NaN propagates.
 __device__ inline float halves_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float halves_sum(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -467,16 +471,17 @@ __device__ inline float halves_sum(float x) {
 }
 
 // Maximum of the NSB * 16 accumulator values of a lane, as four independent
-// running maxima (each folds into v_max3 without operand canonicalisation)
-// combined at the end, so the reduction is not one long dependency chain.
+// running maxima (each folds into v_maximum3) combined at the end, so the
+// reduction is not one long dependency chain.
 template <int NSB>
 __device__ inline float tile_max(const f32x16 (&s)[NSB]) {
   float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) m[e & 3] = fmaxf(m[e & 3], s[sb][e]);
-  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+    for (int e = 0; e < 16; ++e) m[e & 3] = __builtin_elementwise_maximum(m[e & 3], s[sb][e]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[0], m[1]),
+                                       __builtin_elementwise_maximum(m[2], m[3]));
 }
 
 // True in every lane when `pred` holds in at least one lane of the wave.
