@@ -57,12 +57,13 @@ CFLAGS = [
 #                           first fills its destination with NaN
 #   libeiat_attn_alt.so     EIAT_ALT_TILES: other tile shapes
 #   libeiat_attn_timing.so  EIAT_WG_TIMING: per-workgroup start / prologue / end
-#                           stamps of the forward (eiat_wg_times; wg_timeline.py)
+#                           stamps of the forward, dQ and dK/dV (eiat_wg_times,
+#                           eiat_wg_times_dq, eiat_wg_times_dkdv; wg_timeline.py)
 CHECK_BUILDS = {
     "poison": (["-DEIAT_LDS_POISON"],
                ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_decode.hip"]),
     "alt": (["-DEIAT_ALT_TILES"], ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]),
-    "timing": (["-DEIAT_WG_TIMING"], ["attn_fwd.hip"]),
+    "timing": (["-DEIAT_WG_TIMING"], ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]),
 }
 
 

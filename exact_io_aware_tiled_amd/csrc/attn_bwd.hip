@@ -98,6 +98,13 @@ struct DkvCfg {
   static constexpr int SMEM = 2 * BUF + (kVLds ? BNK * NROW : 0);
 };
 
+#ifdef EIAT_WG_TIMING
+// Timing check build: per-workgroup stamps of dK/dV (WgStamps; the prologue
+// ends when the key tile's K and V and the first query tile are in place).
+// Read with eiat_wg_times_dkdv.
+__device__ unsigned long long g_wg_times_dkdv[kWgTimingWords * kWgTimingMax];
+#endif
+
 template <typename T, int D, int MASK, bool DROP>
 __global__ void __launch_bounds__(256)
     __attribute__((amdgpu_waves_per_eu(Elt<T>::kBytes == 2 ? 2 : 1, 8))) attn_bwd_dkdv_kernel(
@@ -113,6 +120,10 @@ __global__ void __launch_bounds__(256)
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
+#ifdef EIAT_WG_TIMING
+  WgStamps wg_stamps;
+  wg_stamps.begin();
+#endif
   const int bh = bid % bh_count;
   int kt = bid / bh_count;
   // Causal: key tiles near the start are seen by the most queries; issue them first.
@@ -131,14 +142,19 @@ __global__ void __launch_bounds__(256)
 
   // This wave's 32 keys of K and V as B-operand chunks (lane: key kw0 + L%32);
   // with kVLds the V rows go to LDS instead and are read back per query tile.
+  // Keys past n read row n - 1: their scores are masked (a wave with such a
+  // key runs only masked tiles) and their dK/dV rows are not stored.  All the
+  // loads are issued here, with the first query tile's, and waited for once:
+  // the sign and zero of c (qmode) are applied after that wait, since an
+  // operation on a loaded value waits for it (and for every load before it).
   u32x4 kf[C::NCH], vf[C::kVLds ? 1 : C::NCH];
+  {
+    const int kr = min(key, n - 1);
 #pragma unroll
-  for (int c = 0; c < C::NCH; ++c) {
-    kf[c] = key < n ? ldg16(Kh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
-    if constexpr (!C::kVLds)
-      vf[c] = key < n ? ldg16(Vh + (int64_t)key * D * C::S + 32 * c + 16 * h) : zero4();
-    if (qmode == 1) kf[c] ^= Elt<T>::kSign;
-    if (qmode == 2) kf[c] = zero4();  // c = 0: every score is exactly 0
+    for (int c = 0; c < C::NCH; ++c) {
+      kf[c] = ldg16(Kh + (int64_t)kr * D * C::S + 32 * c + 16 * h);
+      if constexpr (!C::kVLds) vf[c] = ldg16(Vh + (int64_t)kr * D * C::S + 32 * c + 16 * h);
+    }
   }
   if constexpr (C::kVLds)
     tile_to_lds<32, D * C::S / 16, 1, C::PAD>(smem + C::VRES + 32 * wave * C::NROW, Vh, kw0, n, 0,
@@ -239,6 +255,15 @@ __global__ void __launch_bounds__(256)
     store_tile(0);
   }
   __syncthreads();
+  wait_tile_loads();  // the K / V chunks (when no tile was loaded)
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    if (qmode == 1) kf[c] ^= Elt<T>::kSign;
+    if (qmode == 2) kf[c] = zero4();  // c = 0: every score is exactly 0
+  }
+#ifdef EIAT_WG_TIMING
+  wg_stamps.prologue_done();
+#endif
 
   // Query tiles [ta, tb) need no per-element mask for any key of this wave
   // (every row sees every key); the others straddle a mask boundary or hold
@@ -466,7 +491,22 @@ __global__ void __launch_bounds__(256)
         }
       }
   }
+#ifdef EIAT_WG_TIMING
+  __syncthreads();
+  if (tid == 0) wg_stamps.store(g_wg_times_dkdv, bid);
+#endif
 }
+
+#ifdef EIAT_WG_TIMING
+// Copies the stamps of the last dK/dV launch (layout as eiat_wg_times) to
+// host memory `dst` and the wall clock's rate in kHz to *clock_khz.  Returns a
+// hipError_t code.
+extern "C" __attribute__((visibility("default"))) int eiat_wg_times_dkdv(void* dst, size_t bytes,
+                                                                         int* clock_khz) {
+  return wg_times_copy(HIP_SYMBOL(g_wg_times_dkdv), sizeof(g_wg_times_dkdv), dst, bytes,
+                       clock_khz);
+}
+#endif
 
 // ---------------------------------------------------------------------------
 // launch

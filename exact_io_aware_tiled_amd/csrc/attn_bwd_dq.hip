@@ -52,6 +52,12 @@ struct DqCfg {
   static constexpr int NSB = BN / 32;
 };
 
+#ifdef EIAT_WG_TIMING
+// Timing check build: per-workgroup stamps of dQ (WgStamps; the prologue ends
+// when the first key/value tile is in LDS).  Read with eiat_wg_times_dq.
+__device__ unsigned long long g_wg_times_dq[kWgTimingWords * kWgTimingMax];
+#endif
+
 template <typename T, int D, int MASK, bool DROP>
 __global__ void __launch_bounds__(256)
     __attribute__((amdgpu_waves_per_eu(DqCfg<T, D>::kMinWaves, 8))) attn_bwd_dq_kernel(
@@ -68,6 +74,10 @@ __global__ void __launch_bounds__(256)
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
+#ifdef EIAT_WG_TIMING
+  WgStamps wg_stamps;
+  wg_stamps.begin();
+#endif
   const int bh = bid % bh_count;
   int qt = bid / bh_count;
   if (MASK != 0) qt = num_qtiles - 1 - qt;
@@ -81,34 +91,21 @@ __global__ void __launch_bounds__(256)
   const char* Vh = reinterpret_cast<const char*>(V + head * D);
   const char* dOh = reinterpret_cast<const char*>(dO + head * D);
 
-  u32x4 qf[C::NCH], of[C::NCH];
+  // This row's Q and dO as B-operand chunks, and its O for delta.  Rows past n
+  // read row n - 1: their weights are 0 (LSE taken as +inf) and their dQ and
+  // delta are not stored.  The loads are issued here, with the first key /
+  // value tile's below, and used only after those are issued, since an
+  // operation on a loaded value waits for it (and for every load before it).
+  u32x4 qf[C::NCH], of[C::NCH], oc[C::NCH];
+  const int qr = min(qrow, n - 1);
 #pragma unroll
   for (int c = 0; c < C::NCH; ++c) {
-    qf[c] = qrow < n ? ldg16(Qh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
-    of[c] = qrow < n ? ldg16(dOh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4();
-    if (qmode == 1) qf[c] ^= Elt<T>::kSign;
-    if (qmode == 2) qf[c] = zero4();  // c = 0: every score is exactly 0
+    qf[c] = ldg16(Qh + (int64_t)qr * D * C::S + 32 * c + 16 * h);
+    of[c] = ldg16(dOh + (int64_t)qr * D * C::S + 32 * c + 16 * h);
+    oc[c] = ldg16(reinterpret_cast<const char*>(O + head * D) + (int64_t)qr * D * C::S + 32 * c +
+                  16 * h);
   }
-  const float lse2 = qrow < n ? LSE[head + qrow] * kLog2e : INFINITY;
-  // delta of this row from its O and the dO chunks above (unit 2c + h of the
-  // row is chunk c of half h), summed in unit_dot's tree; written out for the
-  // dK/dV kernel.
-  float dlt;
-  {
-    const char* Oh = reinterpret_cast<const char*>(O + head * D);
-    float u[C::NCH];
-#pragma unroll
-    for (int c = 0; c < C::NCH; ++c)
-      u[c] = unit_dot<T>(qrow < n ? ldg16(Oh + (int64_t)qrow * D * C::S + 32 * c + 16 * h) : zero4(),
-                         of[c]);
-#pragma unroll
-    for (int off = C::NCH / 2; off > 0; off >>= 1)
-#pragma unroll
-      for (int c = 0; c < off; ++c) u[c] += u[c + off];
-    dlt = u[0] + __shfl_xor(u[0], 32, 64);
-    if (qrow >= n) dlt = 0.0f;
-    else if (h == 0) delta[head + qrow] = dlt;
-  }
+  const float lse_row = LSE[head + qr];
   // Dropout (DROP): this row's key of the realized mask.
   const uint32_t row_key = DROP ? drop_row_key(dpar, (uint32_t)bh, (uint32_t)qrow) : 0u;
 
@@ -158,8 +155,33 @@ __global__ void __launch_bounds__(256)
   };
 
   load_tile(t_lo);
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    if (qmode == 1) qf[c] ^= Elt<T>::kSign;
+    if (qmode == 2) qf[c] = zero4();  // c = 0: every score is exactly 0
+  }
+  const float lse2 = qrow < n ? lse_row * kLog2e : INFINITY;
+  // delta of this row from its O and dO chunks (unit 2c + h of the row is
+  // chunk c of half h), summed in unit_dot's tree; written out for the dK/dV
+  // kernel.
+  float dlt;
+  {
+    float u[C::NCH];
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) u[c] = unit_dot<T>(oc[c], of[c]);
+#pragma unroll
+    for (int off = C::NCH / 2; off > 0; off >>= 1)
+#pragma unroll
+      for (int c = 0; c < off; ++c) u[c] += u[c + off];
+    dlt = u[0] + __shfl_xor(u[0], 32, 64);
+    if (qrow >= n) dlt = 0.0f;
+    else if (h == 0) delta[head + qrow] = dlt;
+  }
   store_tile(0);
   __syncthreads();
+#ifdef EIAT_WG_TIMING
+  wg_stamps.prologue_done();
+#endif
 
   for (int t = t_lo; t < t_hi; ++t) {
     const int buf = (t - t_lo) & 1;
@@ -304,7 +326,21 @@ __global__ void __launch_bounds__(256)
         }
       }
   }
+#ifdef EIAT_WG_TIMING
+  __syncthreads();
+  if (tid == 0) wg_stamps.store(g_wg_times_dq, bid);
+#endif
 }
+
+#ifdef EIAT_WG_TIMING
+// Copies the stamps of the last dQ launch (layout as eiat_wg_times) to host
+// memory `dst` and the wall clock's rate in kHz to *clock_khz.  Returns a
+// hipError_t code.
+extern "C" __attribute__((visibility("default"))) int eiat_wg_times_dq(void* dst, size_t bytes,
+                                                                       int* clock_khz) {
+  return wg_times_copy(HIP_SYMBOL(g_wg_times_dq), sizeof(g_wg_times_dq), dst, bytes, clock_khz);
+}
+#endif
 
 // ---------------------------------------------------------------------------
 // dQ launch

@@ -206,9 +206,10 @@ __device__ inline u32x4 fp8_negate(u32x4 w) {
 //   EIAT_ALT_TILES   other tile shapes (keys per streamed tile, query rows per
 //                    dK/dV tile), for the check that results do not depend on
 //                    the block size beyond rounding.
-//   EIAT_WG_TIMING   the forward records per-workgroup wall-clock stamps and
-//                    hardware positions (attn_fwd.hip, eiat_wg_times), for the
-//                    workgroup timeline of a launch; results are unchanged.
+//   EIAT_WG_TIMING   the forward, dQ and dK/dV kernels record per-workgroup
+//                    wall-clock stamps and hardware positions (WgStamps below;
+//                    eiat_wg_times, eiat_wg_times_dq, eiat_wg_times_dkdv), for
+//                    the workgroup timeline of a launch; results are unchanged.
 #ifdef EIAT_ALT_TILES
 constexpr bool kAltTiles = true;
 #else
@@ -578,5 +579,53 @@ __device__ inline bool key_allowed(int q, int j, int n, int window) {
   if constexpr (MASK == 2) ok = ok && (j >= q - window + 1);
   return ok;
 }
+
+#ifdef EIAT_WG_TIMING
+// Timing check build: for every workgroup of a kernel, the constant-rate wall
+// clock (s_memrealtime) at its start, after its prologue and at its end, where
+// it ran (the HW_ID register: CU, shader array and engine; XCC_ID: the XCD),
+// and the shader clock counter (s_memtime) at its start and end, whose
+// difference over the wall-clock difference is the engine clock the workgroup
+// ran at.  Six words per workgroup, for workgroups 0 .. kWgTimingMax - 1, in a
+// table of the kernel's own translation unit.
+constexpr int kWgTimingMax = 1 << 16;
+constexpr int kWgTimingWords = 6;
+struct WgStamps {
+  unsigned long long t0 = 0, c0 = 0, t1 = 0;
+  __device__ void begin() {
+    t0 = __builtin_amdgcn_s_memrealtime();
+    c0 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ void prologue_done() { t1 = __builtin_amdgcn_s_memrealtime(); }
+  // From one thread, after a barrier that ends the workgroup's work.
+  __device__ void store(unsigned long long* table, int bid) const {
+    if (bid >= kWgTimingMax) return;
+    const unsigned long long t2 = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long c2 = __builtin_amdgcn_s_memtime();
+    const unsigned hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID, 32 bits
+    const unsigned xcc_id = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // HW_REG_XCC_ID, 16 bits
+    unsigned long long* rec = table + kWgTimingWords * bid;
+    rec[0] = t0;
+    rec[1] = t1;
+    rec[2] = t2;
+    rec[3] = ((unsigned long long)xcc_id << 32) | hw_id;
+    rec[4] = c0;
+    rec[5] = c2;
+  }
+};
+// Host side: copies a stamp table (the device symbol `table` of `table_bytes`)
+// of the last launch to host memory `dst` (at most `bytes`) and the wall
+// clock's rate in kHz to *clock_khz.  Returns a hipError_t code.
+inline int wg_times_copy(const void* table, size_t table_bytes, void* dst, size_t bytes,
+                         int* clock_khz) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(clock_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(dst, table, bytes < table_bytes ? bytes : table_bytes, 0,
+                            hipMemcpyDeviceToHost);
+  return (int)e;
+}
+#endif
 
 }  // namespace eiat

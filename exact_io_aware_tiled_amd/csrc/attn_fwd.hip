@@ -48,15 +48,8 @@
 namespace eiat {
 
 #ifdef EIAT_WG_TIMING
-// Timing check build: for every workgroup of the forward, the constant-rate
-// wall clock (s_memrealtime) at its start, after its prologue (first score
-// block formed) and at its end, where it ran (the HW_ID register: CU, shader
-// array and engine; XCC_ID: the XCD), and the shader clock counter
-// (s_memtime) at its start and end, whose difference over the wall-clock
-// difference is the engine clock the workgroup ran at.  Read with
-// eiat_wg_times.
-constexpr int kWgTimingMax = 1 << 16;
-constexpr int kWgTimingWords = 6;
+// Timing check build: per-workgroup stamps of the forward (WgStamps; the
+// prologue ends when the first score block is formed).  Read with eiat_wg_times.
 __device__ unsigned long long g_wg_times[kWgTimingWords * kWgTimingMax];
 #endif
 
@@ -153,8 +146,8 @@ __global__ void
   // with masks, the heaviest query tiles (most visible keys) are issued first.
   const int bid = blockIdx.x;
 #ifdef EIAT_WG_TIMING
-  const unsigned long long wg_t0 = __builtin_amdgcn_s_memrealtime();
-  const unsigned long long wg_c0 = __builtin_amdgcn_s_memtime();
+  WgStamps wg_stamps;
+  wg_stamps.begin();
 #endif
   const int bh = bid % bh_count;
   int qt = bid / bh_count;
@@ -608,7 +601,7 @@ __global__ void
   advance_ksw();
   __syncthreads();  // K_lo is overwritten by K_lo+2 in the first iteration
 #ifdef EIAT_WG_TIMING
-  const unsigned long long wg_t1 = __builtin_amdgcn_s_memrealtime();
+  wg_stamps.prologue_done();
 #endif
 
   // Iteration t: the scores of tile t are exponentiated and multiplied into O
@@ -784,19 +777,7 @@ __global__ void
   }
 #ifdef EIAT_WG_TIMING
   __syncthreads();
-  if (tid == 0 && bid < kWgTimingMax) {
-    const unsigned long long wg_t2 = __builtin_amdgcn_s_memrealtime();
-    const unsigned long long wg_c2 = __builtin_amdgcn_s_memtime();
-    const unsigned hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID, 32 bits
-    const unsigned xcc_id = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // HW_REG_XCC_ID, 16 bits
-    unsigned long long* rec = g_wg_times + kWgTimingWords * bid;
-    rec[0] = wg_t0;
-    rec[1] = wg_t1;
-    rec[2] = wg_t2;
-    rec[3] = ((unsigned long long)xcc_id << 32) | hw_id;
-    rec[4] = wg_c0;
-    rec[5] = wg_c2;
-  }
+  if (tid == 0) wg_stamps.store(g_wg_times, bid);
 #endif
 }
 
@@ -848,14 +829,7 @@ static hipError_t launch_fwd_dt(const FwdArgs& a) {
 // code.
 extern "C" __attribute__((visibility("default"))) int eiat_wg_times(void* dst, size_t bytes,
                                                                     int* clock_khz) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(clock_khz, hipDeviceAttributeWallClockRate, dev);
-  if (e == hipSuccess)
-    e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_wg_times),
-                            bytes < sizeof(g_wg_times) ? bytes : sizeof(g_wg_times), 0,
-                            hipMemcpyDeviceToHost);
-  return (int)e;
+  return wg_times_copy(HIP_SYMBOL(g_wg_times), sizeof(g_wg_times), dst, bytes, clock_khz);
 }
 #endif
 

@@ -143,22 +143,26 @@ def test_timing_build(w):
     inp = make_inputs(w, with_grad=True)
     ref = fwd_bwd(A.load_library(), w, inp)
     lib = A.load_check_library("timing")
-    lib.eiat_wg_times.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
-    lib.eiat_wg_times.restype = ctypes.c_int
+    fns = (lib.eiat_wg_times, lib.eiat_wg_times_dq, lib.eiat_wg_times_dkdv)
+    for fn in fns:
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
+        fn.restype = ctypes.c_int
     got = fwd_bwd(lib, w, inp)
-    for name, a, b in zip(("O", "LSE"), got, ref):
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), got, ref):
         assert torch.equal(a, b), name
+    # forward and dQ: 128 query rows per workgroup; dK/dV: 128 keys
     grid = w.B * w.H * ((w.n + 127) // 128)
-    buf = np.zeros(6 * grid, np.uint64)
-    khz = ctypes.c_int(0)
-    assert lib.eiat_wg_times(buf.ctypes.data, buf.nbytes, ctypes.byref(khz)) == 0
-    assert khz.value > 0
-    r = buf.reshape(grid, 6).astype(np.int64)
-    assert (r[:, 0] > 0).all(), "a workgroup left no stamp"
-    assert (r[:, 0] <= r[:, 1]).all() and (r[:, 1] <= r[:, 2]).all()
-    span_us = (r[:, 2].max() - r[:, 0].min()) * 1e3 / khz.value
-    assert 0 < span_us < 1e6
-    assert (r[:, 5] >= r[:, 4]).all()  # shader clock counter, start to end
+    for fn in fns:
+        buf = np.zeros(6 * grid, np.uint64)
+        khz = ctypes.c_int(0)
+        assert fn(buf.ctypes.data, buf.nbytes, ctypes.byref(khz)) == 0
+        assert khz.value > 0
+        r = buf.reshape(grid, 6).astype(np.int64)
+        assert (r[:, 0] > 0).all(), "a workgroup left no stamp"
+        assert (r[:, 0] <= r[:, 1]).all() and (r[:, 1] <= r[:, 2]).all()
+        span_us = (r[:, 2].max() - r[:, 0].min()) * 1e3 / khz.value
+        assert 0 < span_us < 1e6
+        assert (r[:, 5] >= r[:, 4]).all()  # shader clock counter, start to end
 
 
 def test_wg_timeline_summary():
@@ -166,9 +170,11 @@ def test_wg_timeline_summary():
     from exact_io_aware_tiled_amd import wg_timeline
 
     lib = A.load_check_library("timing")
-    lib.eiat_wg_times.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
-    lib.eiat_wg_times.restype = ctypes.c_int
-    announce("wg_timeline smoke")
-    out = wg_timeline.timeline(lib, "smoke", warm_s=0.05)
-    for key in ("span", "slot use", "prologue", "steady rate", "clock"):
-        assert key in out, out
+    for fn in (lib.eiat_wg_times, lib.eiat_wg_times_dq, lib.eiat_wg_times_dkdv):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)]
+        fn.restype = ctypes.c_int
+    for spec in ("smoke", "smoke:dq", "smoke:dkdv"):
+        announce(f"wg_timeline {spec}")
+        out = wg_timeline.timeline(lib, spec, warm_s=0.05)
+        for key in ("span", "slot use", "prologue", "steady rate", "clock"):
+            assert key in out, out

@@ -1,7 +1,7 @@
-"""The key ranges the workgroup timeline fits durations against (CPU)."""
+"""The key and row ranges the workgroup timeline fits durations against (CPU)."""
 import numpy as np
 
-from exact_io_aware_tiled_amd.wg_timeline import BM, visible_keys
+from exact_io_aware_tiled_amd.wg_timeline import BM, BNK, visible_keys, visible_rows
 
 
 def test_visible_keys_match_the_masks():
@@ -18,3 +18,18 @@ def test_visible_keys_match_the_masks():
                 hi = n - 1 if mask == "none" else i
                 keys.update(range(lo, hi + 1))
             assert got[t] == max(keys) - min(keys) + 1, (mask, t)
+
+
+def test_visible_rows_match_the_masks():
+    n, W = 1000, 300
+    kt = np.arange((n + BNK - 1) // BNK)
+    # brute force: the query rows that see any key of the tile, per mask
+    for mask in ("none", "causal", "window"):
+        got = visible_rows(n, mask, W, kt)
+        for t in kt:
+            rows = set()
+            for j in range(t * BNK, min(n, (t + 1) * BNK)):
+                lo = 0 if mask == "none" else j
+                hi = n - 1 if mask != "window" else min(n - 1, j + W - 1)
+                rows.update(range(lo, hi + 1))
+            assert got[t] == max(rows) - min(rows) + 1, (mask, t)
